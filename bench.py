@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the sign-binarised linear layer on one MI355X.
+
+Headline (one JSON line on stdout): the decode GEMV of a Llama-2-7B MLP
+projection, X[1,4096] bf16 (six x60 outlier channels) · W_sign[11008,4096]^T
+with fp16 scales, fp32 output.
+
+* A step is one pass over R layers, each with its own copy of the packed
+  weights and scales (R copies total >= --rotate-gib GiB, so neither L2 nor the
+  256 MB Infinity Cache holds them); the R launches are captured once in a HIP
+  graph and a step is one replay.  Inputs are resident in HBM before timing.
+* value = weight bytes (N·K/8) x R / step time, in GB/s.
+* roofline.achieved = algorithmic bytes of one launch (packed signs + X + a + b
+  + Y) / average launch time over the timed region (HIP events on the stream
+  the graph replays on).
+* cpu_baseline = the fp64 oracle on the same workload, timed on the host.
+* secondary = the other workloads (prefill GEMM TOPS, batched decode, DBF),
+  timed the same way, parity-checked before timing.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "bit_weight_linear_amd", "csrc", name)
+    h = hashlib.sha256()
+    for f in (p, os.path.join(ROOT, "bit_weight_linear_amd", "csrc", "obl_common.hpp")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_src: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    p = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(workload)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def load_binding():
+    try:
+        from bit_weight_linear_amd import binding
+    except ImportError:
+        from bit_weight_linear_amd import build as b
+        log("libobl.so missing: building it")
+        b.build()
+        from bit_weight_linear_amd import binding
+    return binding
+
+
+class Timed:
+    """Captures `launches` (callables) in one HIP graph and times replays."""
+
+    def __init__(self, torch, launches):
+        self.torch = torch
+        for f in launches:            # eager warm-up (allocates library scratch if any)
+            f()
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for f in launches:
+                f()
+        torch.cuda.synchronize()
+        self.n = len(launches)
+
+    def run(self, warmup: int, steps: int):
+        torch = self.torch
+        for _ in range(warmup):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            self.graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop)
+        return ms / steps, ms / (steps * self.n)   # ms per step, ms per launch
+
+
+def onebit_setup(torch, B, WL, O, i, rotate_bytes, check_rows=None, check_cols=None):
+    import numpy as np
+    c = WL.workload(i)
+    dev = torch.device("cuda")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    X = torch.from_numpy(c.X).to(torch.float32).to(tdt[c.x_dtype]).to(dev)
+    a0 = torch.from_numpy(c.a).to(torch.float32).to(tdt[c.scale_dtype]).to(dev)
+    b0 = torch.from_numpy(c.b).to(torch.float32).to(tdt[c.scale_dtype]).to(dev)
+    W0 = B.pack_signs(torch.from_numpy(c.W_sign).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(W0.cpu().numpy().view(np.uint32), O.pack_signs(c.W_sign)), "pack mismatch"
+    per_copy = W0.numel() * 4 + a0.numel() * a0.element_size() + b0.numel() * b0.element_size()
+    R = max(1, -(-rotate_bytes // per_copy))
+    copies = [(W0, a0, b0)] + [(W0.clone(), a0.clone(), b0.clone()) for _ in range(R - 1)]
+    Y = torch.empty((c.M, c.N), dtype=tdt[c.y_dtype], device=dev)
+    # parity of the timed configuration on the first copy
+    B.linear(X, W0, a0, b0, out=Y)
+    torch.cuda.synchronize()
+    Yh = Y.float().cpu().numpy().astype(np.float64)
+    rows = np.arange(c.M) if check_rows is None else check_rows
+    cols = np.arange(c.N) if check_cols is None else check_cols
+    ref = O.onebit_linear(c.X[rows], c.W_sign[cols], c.a[cols], c.b)
+    err = O.max_normalised_error(Yh[np.ix_(rows, cols)], ref, O.onebit_error_scale(c.X[rows], c.a[cols], c.b))
+    launches = [(lambda W=W, a=a, b=b: B.linear(X, W, a, b, out=Y)) for (W, a, b) in copies]
+    return c, launches, err, R
+
+
+def dbf_setup(torch, B, WL, O, rotate_bytes):
+    import numpy as np
+    c = WL.workload(5)
+    dev = torch.device("cuda")
+    X = torch.from_numpy(c.X).to(torch.float32).to(torch.bfloat16).to(dev)
+    sc = [torch.from_numpy(v).to(torch.float32).to(torch.float16).to(dev) for v in (c.b, c.m, c.a)]
+    S2 = B.pack_signs(torch.from_numpy(c.S2).to(dev))
+    S1 = B.pack_signs(torch.from_numpy(c.S1).to(dev))
+    per_copy = (S2.numel() + S1.numel()) * 4 + sum(t.numel() * 2 for t in sc)
+    R = max(1, -(-rotate_bytes // per_copy))
+    copies = [(S2, S1, *sc)] + [(S2.clone(), S1.clone(), *[t.clone() for t in sc]) for _ in range(R - 1)]
+    Y = torch.empty((c.M, c.N), dtype=torch.float32, device=dev)
+    ws = torch.empty((c.M, c.Kmid), dtype=torch.float32, device=dev)
+    B.dbf_linear(X, S2, S1, *sc, workspace=ws, out=Y)
+    torch.cuda.synchronize()
+    err = O.max_normalised_error(Y.cpu().numpy().astype(np.float64),
+                                 O.dbf_linear(c.X, c.S1, c.S2, c.a, c.m, c.b),
+                                 O.dbf_error_scale(c.X, c.b, c.m, c.a))
+    launches = [(lambda s2=s2, s1=s1, b=b, m=m, a=a: B.dbf_linear(X, s2, s1, b, m, a, workspace=ws, out=Y))
+                for (s2, s1, b, m, a) in copies]
+    return c, launches, err, R
+
+
+def cpu_baseline(WL, O, budget_s: float = 12.0):
+    """Time the fp64 oracle on workload 2 (the headline) for a bounded sample."""
+    import numpy as np
+    c = WL.workload(2)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 50):
+        t0 = time.perf_counter()
+        O.onebit_linear(c.X, c.W_sign, c.a, c.b)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    wbytes = c.N * c.K / 8
+    return {"value": round(wbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full calls of workload 1x4096x11008 (fp64 dense W = W_sign*(a b^T) "
+                      f"then X W^T), median {t * 1e3:.1f} ms per call; weight bytes N*K/8 per call; "
+                      f"dense-W formation is single-threaded NumPy, the product uses {threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from bit_weight_linear_amd import workloads as WL
+
+    B = load_binding()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rot = int(args.rotate_gib * (1 << 30))
+
+    # ---------------- headline: workload 2, M = 1 decode GEMV
+    c, launches, err, R = onebit_setup(torch, B, WL, O, 2, rot)
+    log(f"[bench] {c.name}: parity max normalised error {err:.3e}; {R} weight copies")
+    assert err <= 1e-5, "parity failed on the timed configuration"
+    t = Timed(torch, launches)
+    ms_step, ms_launch = t.run(args.warmup, args.steps)
+    wbytes = c.N * c.K // 8
+    alg_bytes = wbytes + c.M * c.K * 2 + c.N * 2 + c.K * 2 + c.M * c.N * 4
+    value = wbytes * R / (ms_step * 1e-3) / 1e9
+    achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
+    traffic = measured_traffic("gemv_lut.hip", "decode-gemv-1x4096x11008")
+    out = {
+        "metric": "1-bit linear: weight GB/s (% HBM peak) at M=1; TOPS (% MFMA peak) at M=2048",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": c.name, "M": c.M, "K": c.K, "N": c.N, "x_dtype": c.x_dtype,
+                   "scale_dtype": c.scale_dtype, "y_dtype": c.y_dtype, "layers_per_step": R,
+                   "weight_bytes_per_layer": wbytes, "parallelism": "single-gpu",
+                   "step": f"{R} launches over distinct weight copies, one HIP graph replay"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "us_per_launch": round(ms_launch * 1e3, 4),
+        "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
+        "parity_max_normalised_error": float(f"{err:.3e}"),
+    }
+    del launches, t
+    torch.cuda.empty_cache()
+
+    # ---------------- secondary workloads
+    if not args.no_secondary:
+        sec = {}
+        rng = np.random.default_rng(0)
+        # workload 4: prefill GEMM, M = 2048
+        rows = np.unique(np.concatenate([rng.choice(2048, 32, replace=False), [0, 2047]]))
+        cols = np.unique(np.concatenate([rng.choice(14336, 96, replace=False), [0, 14335]]))
+        c4, l4, e4, R4 = onebit_setup(torch, B, WL, O, 4, min(rot, 64 << 20), rows, cols)
+        assert e4 <= 8e-3, "parity failed on workload 4"
+        t4 = Timed(torch, l4)
+        ms4_step, ms4 = t4.run(2, max(3, args.steps // 4))
+        flops = 2.0 * c4.M * c4.N * c4.K
+        tflops = flops / (ms4 * 1e-3) / 1e12
+        sec[c4.name] = {"us_per_launch": round(ms4 * 1e3, 2), "TOPS": round(tflops, 2),
+                        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
+                        "parity_max_normalised_error_sampled": float(f"{e4:.3e}"), "copies": R4}
+        log(f"[bench] {c4.name}: {ms4 * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+        del l4, t4
+        torch.cuda.empty_cache()
+        # workloads 1, 3: decode kernel
+        for i in (3, 1):
+            ci, li, ei, Ri = onebit_setup(torch, B, WL, O, i, rot if i == 3 else (64 << 20))
+            assert ei <= 1e-5, f"parity failed on workload {i}"
+            ti = Timed(torch, li)
+            _, msi = ti.run(args.warmup, args.steps)
+            wb = ci.N * ci.K / 8
+            sec[ci.name] = {"us_per_launch": round(msi * 1e3, 3),
+                            "weight_GBps": round(wb / (msi * 1e-3) / 1e9, 1),
+                            "parity_max_normalised_error": float(f"{ei:.3e}"), "copies": Ri}
+            log(f"[bench] {ci.name}: {msi * 1e3:.2f} us")
+            del li, ti
+        # workload 5: DBF
+        c5, l5, e5, R5 = dbf_setup(torch, B, WL, O, rot)
+        assert e5 <= 1e-5, "parity failed on workload 5"
+        t5 = Timed(torch, l5)
+        _, ms5 = t5.run(args.warmup, args.steps)
+        wb5 = c5.Kmid * (c5.K + c5.N) / 8
+        sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
+                        "parity_max_normalised_error": float(f"{e5:.3e}"), "copies": R5,
+                        "launches_per_call": 2}
+        log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
+        del l5, t5
+        out["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(WL, O)
+        log(f"[bench] cpu baseline {out['cpu_baseline']['value']} GB/s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

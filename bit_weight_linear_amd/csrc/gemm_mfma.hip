@@ -1,0 +1,261 @@
+// Prefill contraction for M > 16 on bf16 matrix cores:
+// Y = ((X ⊙ b) W_sign^T) ⊙ a with fp32 accumulation.
+//
+// OneBit page ("1bit量化"), proposition 1; for M > 16 this is a dense
+// contraction (2·M·N·K flops), so it runs on v_mfma_f32_16x16x32_bf16.
+//
+// Operands per 32-k step, in pair order (obl_common.hpp):
+//  * B (weights) is never stored as bf16 anywhere: each wave reads packed sign
+//    words from LDS and expands them in registers -- one shift and one
+//    v_bitop3 per two weights -- into +-m_k, where m_k is bf16(b_k) when the
+//    input-side scale is folded into B ("raw" A mode) or 1.0 otherwise.
+//  * A (activations) is staged in LDS already in pair order, one 16-byte
+//    fragment per lane, so each A fragment is a single ds_read_b128.
+//      raw mode     (X bf16):  A = x exactly; b is folded into B as bf16(b).
+//      convert mode (X fp32, or no b):  A = bf16(x·b) (or bf16(x)), B = +-1.
+//    Either way each product carries one bf16 rounding of one input-side
+//    factor (relative error <= 2^-8), products are exact in fp32 and the
+//    accumulation is fp32.
+//  * Epilogue: acc·a in fp32, one cast to the output dtype.
+//
+// Tiling: 256 x 224 block tile, 8 waves as 4 (M) x 2 (N), 64 x 112 per wave
+// (4 x 7 fragments, 112 fp32 accumulators per lane), K staged 64 at a time in
+// double-buffered LDS.  For M = 2048, N = 14336 this gives 8 x 64 = 512 tiles,
+// exactly two per CU on 256 CUs.  Workgroups are dispatched round-robin over
+// the 8 XCDs, so the tile order puts all tiles of one block-row on one XCD:
+// that XCD's L2 then holds the shared activation rows.
+#include "obl_common.hpp"
+#include "obl_internal.hpp"
+
+namespace obl {
+namespace {
+
+constexpr int GM_BM = 256;
+constexpr int GM_BN = 224;
+constexpr int GM_KT = 64;
+constexpr int GM_STEPS = GM_KT / 32;
+constexpr int GM_THREADS = 512;
+constexpr int GM_FM = 4;   // A fragments per wave (64 rows)
+constexpr int GM_FN = 7;   // B fragments per wave (112 columns)
+constexpr int GM_SLOTS = GM_STEPS * (GM_BM / 16) * 64;  // A fragment slots per stage
+constexpr int GM_SLOTS_PER_THREAD = GM_SLOTS / GM_THREADS;
+
+enum AMode { A_RAW = 0, A_CONVERT = 1 };
+
+struct GemmSmem {
+  u32x4 a[2][GM_STEPS][GM_BM / 16][64];
+  uint32_t bw[2][GM_BN][GM_STEPS];
+  u32x4 mag[2][GM_STEPS][4];
+};
+
+// Two 4-element runs r0 = (v0..v3), r1 = (v16..v19) of bf16 -> pair order
+// dwords (v_j, v_{16+j}).
+__device__ __forceinline__ u32x4 interleave_pairs(u32x2 r0, u32x2 r1) {
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(r1.x, r0.x, 0x05040100u);
+  o.y = __builtin_amdgcn_perm(r1.x, r0.x, 0x07060302u);
+  o.z = __builtin_amdgcn_perm(r1.y, r0.y, 0x05040100u);
+  o.w = __builtin_amdgcn_perm(r1.y, r0.y, 0x07060302u);
+  return o;
+}
+
+template <int AMODE, typename XT, typename ST, bool PRE>
+struct Stager {
+  // Registers holding one stage of global data before it is written to LDS.
+  u32x4 a[GM_SLOTS_PER_THREAD];
+  uint32_t bw;
+  u32x4 mag;
+
+  __device__ __forceinline__ void load(const XT* __restrict__ X, int64_t M, int64_t K,
+                                       const uint32_t* __restrict__ W, int64_t N,
+                                       const ST* __restrict__ pre, int64_t m0, int64_t n0,
+                                       int64_t kt, int tid) {
+    const int64_t kw = K >> 5;
+    // A slots: slot = tid + 512 i -> (t, row, g) with g fastest.
+#pragma unroll
+    for (int i = 0; i < GM_SLOTS_PER_THREAD; ++i) {
+      const int slot = tid + GM_THREADS * i;
+      const int g = slot & 3;
+      const int row = (slot >> 2) & (GM_BM - 1);
+      const int t = slot >> 10;
+      const int64_t gr = m0 + row;
+      const int64_t step = kt * GM_STEPS + t;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (gr < M && step < kw) {
+        const int64_t kb = step * 32 + 4 * g;
+        const XT* xr = X + gr * K + kb;
+        if constexpr (AMODE == A_RAW) {
+          const u32x2 r0 = *reinterpret_cast<const u32x2*>(xr);
+          const u32x2 r1 = *reinterpret_cast<const u32x2*>(xr + 16);
+          v = interleave_pairs(r0, r1);
+        } else {
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float lo = to_f32(xr[j]), hi = to_f32(xr[j + 16]);
+            if (PRE) {
+              lo *= to_f32(pre[kb + j]);
+              hi *= to_f32(pre[kb + j + 16]);
+            }
+            d[j] = pack_bf16_pair(lo, hi);
+          }
+          v = u32x4{d[0], d[1], d[2], d[3]};
+        }
+      }
+      a[i] = v;
+    }
+    // Sign words: thread -> (column, step).
+    bw = 0u;
+    if (tid < GM_BN * GM_STEPS) {
+      const int c = tid >> 1, t = tid & 1;
+      const int64_t n = n0 + c, step = kt * GM_STEPS + t;
+      if (n < N && step < kw) bw = W[n * kw + step];
+    }
+    // Magnitudes of B in raw mode: bf16(b) pairs per (step, lane group).
+    if constexpr (AMODE == A_RAW && PRE) {
+      const int r = tid - GM_BN * GM_STEPS;
+      mag = u32x4{0u, 0u, 0u, 0u};
+      if (r >= 0 && r < GM_STEPS * 4) {
+        const int t = r >> 2, g = r & 3;
+        const int64_t step = kt * GM_STEPS + t;
+        if (step < kw) {
+          const int64_t kb = step * 32 + 4 * g;
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d[j] = pack_bf16_pair(to_f32(pre[kb + j]), to_f32(pre[kb + j + 16]));
+          mag = u32x4{d[0], d[1], d[2], d[3]};
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(GemmSmem& sm, int buf, int tid) const {
+#pragma unroll
+    for (int i = 0; i < GM_SLOTS_PER_THREAD; ++i) {
+      const int slot = tid + GM_THREADS * i;
+      const int g = slot & 3;
+      const int row = (slot >> 2) & (GM_BM - 1);
+      const int t = slot >> 10;
+      sm.a[buf][t][row >> 4][16 * g + (row & 15)] = a[i];
+    }
+    if (tid < GM_BN * GM_STEPS) sm.bw[buf][tid >> 1][tid & 1] = bw;
+    if (AMODE == A_RAW && PRE) {
+      const int r = tid - GM_BN * GM_STEPS;
+      if (r >= 0 && r < GM_STEPS * 4) sm.mag[buf][r >> 2][r & 3] = mag;
+    }
+  }
+};
+
+template <int AMODE, typename XT, typename ST, typename YT, bool PRE>
+__global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(
+    const XT* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
+    const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, int mt, int nt,
+    int xcd_groups) {
+  __shared__ GemmSmem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4;
+
+  // Tile order: with xcd_groups = 8, XCD x (= blockIdx % 8) gets the
+  // contiguous tile range [x·T/8, (x+1)·T/8), row-major over (tm, tn).
+  int lin = blockIdx.x;
+  if (xcd_groups > 1) {
+    const int per = (mt * nt) / xcd_groups;
+    lin = (blockIdx.x % xcd_groups) * per + blockIdx.x / xcd_groups;
+  }
+  const int tm = lin / nt, tn = lin - (lin / nt) * nt;
+  const int64_t m0 = (int64_t)tm * GM_BM, n0 = (int64_t)tn * GM_BN;
+  const int64_t kw = K >> 5;
+  const int64_t nk = (kw + GM_STEPS - 1) / GM_STEPS;
+
+  f32x4 acc[GM_FM][GM_FN];
+#pragma unroll
+  for (int i = 0; i < GM_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < GM_FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Stager<AMODE, XT, ST, PRE> st;
+  st.load(X, M, K, W, N, pre, m0, n0, 0, tid);
+  st.store(sm, 0, tid);
+  __syncthreads();
+
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) st.load(X, M, K, W, N, pre, m0, n0, kt + 1, tid);
+#pragma unroll
+    for (int t = 0; t < GM_STEPS; ++t) {
+      u32x4 af[GM_FM];
+#pragma unroll
+      for (int i = 0; i < GM_FM; ++i) af[i] = sm.a[buf][t][wm * GM_FM + i][lane];
+      const u32x4 mag = (AMODE == A_RAW && PRE) ? sm.mag[buf][t][g] : ones;
+#pragma unroll
+      for (int j = 0; j < GM_FN; ++j) {
+        const uint32_t w = sm.bw[buf][wn * (GM_FN * 16) + j * 16 + (lane & 15)][t];
+        const u32x4 bf = expand_signs_scaled(w >> (4 * g), mag);
+#pragma unroll
+        for (int i = 0; i < GM_FM; ++i) acc[i][j] = mfma16x16x32(af[i], bf, acc[i][j]);
+      }
+    }
+    if (kt + 1 < nk) st.store(sm, buf ^ 1, tid);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds rows 4g..4g+3 of column (lane & 15) of each fragment.
+#pragma unroll
+  for (int j = 0; j < GM_FN; ++j) {
+    const int64_t n = n0 + wn * (GM_FN * 16) + j * 16 + (lane & 15);
+    if (n >= N) continue;
+    const float s = to_f32(post[n]);
+#pragma unroll
+    for (int i = 0; i < GM_FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * (GM_FM * 16) + i * 16 + 4 * g + r;
+        if (m < M) Store<YT>::put(&Y[m * N + n], acc[i][j][r] * s);
+      }
+    }
+  }
+}
+
+template <int AMODE, typename XT, typename ST, typename YT, bool PRE>
+hipError_t launch_t(const LinearArgs& a, const DeviceInfo&) {
+  const int64_t mt = (a.M + GM_BM - 1) / GM_BM;
+  const int64_t nt = (a.N + GM_BN - 1) / GM_BN;
+  const int64_t tiles = mt * nt;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const int xcd = (tiles % 8 == 0) ? 8 : 1;
+  hipLaunchKernelGGL((gemm_mfma_kernel<AMODE, XT, ST, YT, PRE>), dim3((unsigned)tiles),
+                     dim3(GM_THREADS), 0, a.stream, static_cast<const XT*>(a.X), a.M, a.K, a.W, a.N,
+                     static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post),
+                     static_cast<YT*>(a.Y), (int)mt, (int)nt, xcd);
+  return hipGetLastError();
+}
+
+template <typename ST, typename YT>
+hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
+  // bf16 activations (8-byte aligned rows): A = x exactly, and the input-side
+  // scale, if any, is folded into B as bf16(b).  Otherwise A is converted once
+  // per staged element: bf16(x·b) or bf16(x).
+  const bool raw = a.x_dtype == DT_BF16 && (reinterpret_cast<uintptr_t>(a.X) % 8 == 0);
+  if (raw) return a.pre ? launch_t<A_RAW, bf16_t, ST, YT, true>(a, dev)
+                        : launch_t<A_RAW, bf16_t, ST, YT, false>(a, dev);
+  if (a.x_dtype == DT_BF16) return a.pre ? launch_t<A_CONVERT, bf16_t, ST, YT, true>(a, dev)
+                                         : launch_t<A_CONVERT, bf16_t, ST, YT, false>(a, dev);
+  return a.pre ? launch_t<A_CONVERT, float, ST, YT, true>(a, dev)
+               : launch_t<A_CONVERT, float, ST, YT, false>(a, dev);
+}
+template <typename ST>
+hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.y_dtype == DT_F32 ? launch_mode<ST, float>(a, dev) : launch_mode<ST, bf16_t>(a, dev);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.scale_dtype == DT_F32 ? launch_y<float>(a, dev) : launch_y<f16_t>(a, dev);
+}
+
+}  // namespace obl

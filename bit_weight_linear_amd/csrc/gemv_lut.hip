@@ -1,0 +1,208 @@
+// Decode GEMV for M <= 2 rows: Y = ((X ⊙ b) W_sign^T) ⊙ a in fp32.
+//
+// OneBit page ("1bit量化"), proposition 1: the contraction with W_sign only
+// adds or subtracts x_k b_k; a is applied once per output.  The DBF page
+// ("Methodologie") makes the same point: the binary matrices turn the
+// multiplications into additions.
+//
+// Design (bandwidth-bound at M = 1; every sign bit is read once from HBM):
+//  * The sign additions are regrouped four k at a time.  For a group of four
+//    inputs x'_4g..x'_4g+3 (x' = x ⊙ b in fp32) a table holds all 16 signed
+//    sums  T[n] = Σ_i (bit i of n ? -x'_i : x'_i).  One nibble of a packed
+//    sign word then selects the sum of its four signed terms: one bit-field
+//    extract, one LDS read and one fp32 add replace four conditional adds.
+//  * The table (one per input row) is built by the block in LDS from X and b
+//    for a 4096-k slab: 1024 groups x 16 entries.  Group (c, q) -- chunk c of
+//    128 k, nibble q of that chunk -- lives in dword column 33c + q of each
+//    16-entry row, so the 32 lanes of a half-wave (c = 0..31, same q) hit 32
+//    different banks whatever nibbles they read.
+//  * Lane l of a half-wave owns chunk c = l % 32 (4 sign words, one 128-bit
+//    coalesced load per row); a half-wave walks whole rows.  The sign loads are
+//    issued before the table build so their HBM latency overlaps it.
+//  * Per-lane partial sums are reduced across the 32 lanes with DPP
+//    (quad_perm, half-mirror, mirror) plus one swizzle, in a fixed order, so
+//    results are bitwise reproducible.  No atomics.
+#include "obl_common.hpp"
+#include "obl_internal.hpp"
+
+namespace obl {
+namespace {
+
+constexpr int LUT_THREADS = 1024;
+constexpr int LUT_HALFWAVES = LUT_THREADS / 32;  // 32
+constexpr int LUT_SLAB_K = 4096;                 // 32 chunks x 128 k
+constexpr int LUT_COLS = 33 * 32;                // padded columns per nibble row
+constexpr int LUT_RPH = 4;                       // rows per half-wave (max)
+constexpr int LUT_MAX_ROWS = LUT_HALFWAVES * LUT_RPH;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 32 lanes of each half-wave; every lane receives the total.
+__device__ __forceinline__ float halfwave_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror: combine the two quads of each 8
+  v += dpp_mov<0x140>(v);  // row_mirror: combine the two 8-lane halves of each row
+  v += __shfl_xor(v, 16);  // combine the two 16-lane rows of the half-wave
+  return v;
+}
+
+template <int MR, typename XT, typename ST, typename YT, bool PRE, bool VEC4>
+__global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
+    const XT* __restrict__ X, int64_t K, const uint32_t* __restrict__ W, int64_t N,
+    const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y,
+    int rows_per_block) {
+  // lut[(nib * LUT_COLS + col) * MR + m]: one 16-entry table per group and row.
+  __shared__ float lut[16 * LUT_COLS * MR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int hw = tid >> 5;
+  const int c = lane & 31;
+  const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+  const int nrows = (int)min((int64_t)rows_per_block, N - row0);
+  const int64_t kw = K >> 5;
+
+  float acc[LUT_RPH][MR];
+#pragma unroll
+  for (int r = 0; r < LUT_RPH; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+
+  for (int64_t s0 = 0; s0 < K; s0 += LUT_SLAB_K) {
+    // 1. Sign words of this lane's chunk for each of its rows.
+    const int64_t w0 = (s0 >> 5) + 4 * c;
+    u32x4 wv[LUT_RPH];
+#pragma unroll
+    for (int r = 0; r < LUT_RPH; ++r) {
+      const int row = hw + LUT_HALFWAVES * r;
+      wv[r] = u32x4{0u, 0u, 0u, 0u};
+      if (row < nrows) {
+        const uint32_t* src = W + (row0 + row) * kw + w0;
+        if (VEC4) {
+          if (w0 < kw) wv[r] = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          if (w0 + 0 < kw) wv[r].x = src[0];
+          if (w0 + 1 < kw) wv[r].y = src[1];
+          if (w0 + 2 < kw) wv[r].z = src[2];
+          if (w0 + 3 < kw) wv[r].w = src[3];
+        }
+      }
+    }
+
+    // 2. Table for this slab.  Thread tid owns group g = tid (k = s0 + 4g ..).
+    if (s0 > 0) __syncthreads();  // the previous slab's lookups are done
+    {
+      const int g = tid;
+      const int64_t k = s0 + 4 * g;
+      const int col = 33 * (g >> 5) + (g & 31);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = 0.f;
+          if (k + i < K) {
+            v = to_f32(X[m * K + k + i]);
+            if (PRE) v *= to_f32(pre[k + i]);
+          }
+          x[i] = v;
+        }
+        // bit i of the nibble set -> -x_i.  p indexed by bits (0,1), q by bits (2,3).
+        const float p0 = x[0] + x[1], p2 = x[0] - x[1];
+        const float q0 = x[2] + x[3], q2 = x[2] - x[3];
+        const float p[4] = {p0, -p2, p2, -p0};
+        const float q[4] = {q0, -q2, q2, -q0};
+#pragma unroll
+        for (int n = 0; n < 16; ++n) lut[(n * LUT_COLS + col) * MR + m] = p[n & 3] + q[n >> 2];
+      }
+    }
+    __syncthreads();
+
+    // 3. Lookups: one nibble -> one signed 4-term sum per input row.
+    const int cbase = 33 * c;
+#pragma unroll
+    for (int r = 0; r < LUT_RPH; ++r) {
+      if (hw + LUT_HALFWAVES * r < nrows) {
+        const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const uint32_t nib = (words[q >> 3] >> ((q & 7) * 4)) & 15u;
+          const float* e = &lut[(nib * LUT_COLS + cbase + q) * MR];
+#pragma unroll
+          for (int m = 0; m < MR; ++m) acc[r][m] += e[m];
+        }
+      }
+    }
+  }
+
+  // 4. Reduce across the half-wave and write the scaled outputs.
+#pragma unroll
+  for (int r = 0; r < LUT_RPH; ++r) {
+    const int row = hw + LUT_HALFWAVES * r;
+    float tot[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) tot[m] = halfwave_sum(acc[r][m]);
+    if (c == 0 && row < nrows) {
+      const int64_t n = row0 + row;
+      const float s = to_f32(post[n]);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) Store<YT>::put(&Y[m * N + n], tot[m] * s);
+    }
+  }
+}
+
+template <int MR, typename XT, typename ST, typename YT, bool PRE>
+hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
+  int64_t blocks = dev.num_cus;
+  int64_t rpb = (a.N + blocks - 1) / blocks;
+  if (rpb < 16) rpb = a.N < 16 ? a.N : 16;          // amortise the table over >= 16 rows
+  if (rpb > LUT_MAX_ROWS) rpb = LUT_MAX_ROWS;
+  blocks = (a.N + rpb - 1) / rpb;
+  const bool vec4 = (a.K % 128 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0);
+  auto X = static_cast<const XT*>(a.X);
+  auto pre = static_cast<const ST*>(a.pre);
+  auto post = static_cast<const ST*>(a.post);
+  auto Y = static_cast<YT*>(a.Y);
+  if (vec4)
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, XT, ST, YT, PRE, true>), dim3((unsigned)blocks),
+                       dim3(LUT_THREADS), 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, (int)rpb);
+  else
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, XT, ST, YT, PRE, false>), dim3((unsigned)blocks),
+                       dim3(LUT_THREADS), 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, (int)rpb);
+  return hipGetLastError();
+}
+
+template <int MR, typename XT, typename ST, typename YT>
+hipError_t launch_pre(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.pre ? launch_t<MR, XT, ST, YT, true>(a, dev) : launch_t<MR, XT, ST, YT, false>(a, dev);
+}
+
+template <int MR, typename XT, typename ST>
+hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.y_dtype == DT_F32 ? launch_pre<MR, XT, ST, float>(a, dev)
+                             : launch_pre<MR, XT, ST, bf16_t>(a, dev);
+}
+
+template <int MR, typename XT>
+hipError_t launch_s(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.scale_dtype == DT_F32 ? launch_y<MR, XT, float>(a, dev) : launch_y<MR, XT, f16_t>(a, dev);
+}
+
+template <int MR>
+hipError_t launch_x(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.x_dtype == DT_F32 ? launch_s<MR, float>(a, dev) : launch_s<MR, bf16_t>(a, dev);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_lut(const LinearArgs& a, const DeviceInfo& dev) {
+  if (a.M == 1) return launch_x<1>(a, dev);
+  if (a.M == 2) return launch_x<2>(a, dev);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace obl

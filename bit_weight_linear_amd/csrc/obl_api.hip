@@ -1,0 +1,274 @@
+// C ABI of libobl: argument validation, path dispatch and per-device scratch.
+//
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state (and the error paths can be exercised without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_map>
+
+#include "../../include/obl.h"
+#include "obl_internal.hpp"
+
+namespace obl {
+namespace {
+
+constexpr int64_t kMaxBytes = int64_t(1) << 62;
+
+int elem_size(obl_dtype d) {
+  switch (d) {
+    case OBL_F32: return 4;
+    case OBL_F16: return 2;
+    case OBL_BF16: return 2;
+    case OBL_I8: return 1;
+  }
+  return 0;
+}
+
+bool valid_dtype(int d) { return d >= OBL_F32 && d <= OBL_I8; }
+
+// a*b*c bytes without overflow past 2^62; returns -1 when too large.
+int64_t checked_bytes(int64_t a, int64_t b, int64_t c) {
+  if (a < 0 || b < 0 || c < 0) return -1;
+  __int128 v = (__int128)a * b * c;
+  return v >= kMaxBytes ? -1 : (int64_t)v;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Range a, Range b) {
+  if (a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, int64_t n) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)n) == 0; }
+
+// Path selection.  OBL_PATH=lut|decode|gemm forces a path (tests use this to
+// cover every kernel at every M it supports); unset or "auto" picks by M.
+enum Path { P_AUTO, P_LUT, P_DECODE, P_GEMM };
+Path forced_path() {
+  const char* s = std::getenv("OBL_PATH");
+  if (!s || !*s || !std::strcmp(s, "auto")) return P_AUTO;
+  if (!std::strcmp(s, "lut")) return P_LUT;
+  if (!std::strcmp(s, "decode")) return P_DECODE;
+  if (!std::strcmp(s, "gemm")) return P_GEMM;
+  return P_AUTO;
+}
+
+Path choose_path(int64_t M, obl_status* st) {
+  Path p = forced_path();
+  if (p == P_AUTO) {
+    if (M <= kLutMaxM) return P_LUT;
+    if (M <= kDecodeMaxM) return P_DECODE;
+    return P_GEMM;
+  }
+  if ((p == P_LUT && M > kLutMaxM) || (p == P_DECODE && M > kDecodeMaxM)) *st = OBL_ERR_SHAPE;
+  return p;
+}
+
+std::mutex g_mu;
+std::unordered_map<int, DeviceInfo> g_info;
+std::unordered_map<int, Scratch> g_scratch;
+
+obl_status run_linear(const LinearArgs& la, Path path) {
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+  hipError_t e;
+  switch (path) {
+    case P_LUT: e = launch_gemv_lut(la, dev); break;
+    case P_DECODE: e = launch_decode_mfma(la, dev); break;
+    default: e = launch_gemm_mfma(la, dev); break;
+  }
+  if (e != hipSuccess) return OBL_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+  return OBL_OK;
+}
+
+bool linear_dtypes_ok(obl_dtype x, obl_dtype s, obl_dtype y) {
+  return (x == OBL_F32 || x == OBL_BF16) && (s == OBL_F32 || s == OBL_F16) &&
+         (y == OBL_F32 || y == OBL_BF16);
+}
+
+}  // namespace
+
+hipError_t device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_info.find(dev);
+  if (it == g_info.end()) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    it = g_info.emplace(dev, DeviceInfo{dev, cus > 0 ? cus : 1}).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
+hipError_t scratch_reserve(int device, size_t partial_floats, size_t n_counters, Scratch* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Scratch& s = g_scratch[device];
+  if (s.partial_floats >= partial_floats && s.n_counters >= n_counters) {
+    *out = s;
+    return hipSuccess;
+  }
+  size_t pf = partial_floats > s.partial_floats ? partial_floats : s.partial_floats;
+  size_t nc = n_counters > s.n_counters ? n_counters : s.n_counters;
+  if (pf < (size_t(8) << 20)) pf = size_t(8) << 20;  // 32 MiB of partial sums
+  if (nc < 65536) nc = 65536;
+  if (s.partials) {
+    // Work already enqueued may still use the old buffers.
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    (void)hipFree(s.partials);
+    (void)hipFree(s.counters);
+    s = Scratch{};
+  }
+  float* p = nullptr;
+  unsigned* c = nullptr;
+  hipError_t e = hipMalloc(&p, pf * sizeof(float));
+  if (e != hipSuccess) return e;
+  e = hipMalloc(&c, nc * sizeof(unsigned));
+  if (e != hipSuccess) { (void)hipFree(p); return e; }
+  e = hipMemset(c, 0, nc * sizeof(unsigned));  // counters start (and are left) at zero
+  if (e != hipSuccess) { (void)hipFree(p); (void)hipFree(c); return e; }
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  s = Scratch{p, pf, c, nc};
+  *out = s;
+  return hipSuccess;
+}
+
+}  // namespace obl
+
+using namespace obl;
+
+extern "C" {
+
+const char* obl_status_string(obl_status s) {
+  switch (s) {
+    case OBL_OK: return "OBL_OK";
+    case OBL_ERR_NULL: return "OBL_ERR_NULL: a required pointer is NULL";
+    case OBL_ERR_SHAPE: return "OBL_ERR_SHAPE: invalid dimension";
+    case OBL_ERR_DTYPE: return "OBL_ERR_DTYPE: unsupported dtype combination";
+    case OBL_ERR_ALIGN: return "OBL_ERR_ALIGN: misaligned pointer";
+    case OBL_ERR_ALIAS: return "OBL_ERR_ALIAS: output overlaps another argument";
+    case OBL_ERR_HIP: return "OBL_ERR_HIP: HIP runtime error";
+    case OBL_ERR_INTERNAL: return "OBL_ERR_INTERNAL: internal error";
+  }
+  return "OBL_ERR_UNKNOWN";
+}
+
+int obl_version(void) { return 100; }  // 0.1.0
+
+obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_t K,
+                          uint32_t* packed, void* stream) {
+  try {
+    if (!S || !packed) return OBL_ERR_NULL;
+    if (rows < 1 || K < 1 || K % 32 != 0) return OBL_ERR_SHAPE;
+    if (!valid_dtype(s_dtype)) return OBL_ERR_DTYPE;
+    int64_t sb = checked_bytes(rows, K, elem_size(s_dtype));
+    int64_t pb = checked_bytes(rows, K / 32, 4);
+    if (sb < 0 || pb < 0) return OBL_ERR_SHAPE;
+    if (!aligned(S, elem_size(s_dtype)) || !aligned(packed, 4)) return OBL_ERR_ALIGN;
+    if (overlap(range_of(S, sb), range_of(packed, pb))) return OBL_ERR_ALIAS;
+    hipError_t e = launch_pack_signs(S, s_dtype, rows, K, packed, (hipStream_t)stream);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+    return OBL_OK;
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
+obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                      const uint32_t* W_packed, int64_t N,
+                      const void* a, const void* b, obl_dtype scale_dtype,
+                      void* Y, obl_dtype y_dtype, void* stream) {
+  try {
+    if (M < 0 || K < 1 || N < 1 || K % 32 != 0) return OBL_ERR_SHAPE;
+    if (!W_packed || !a || !b) return OBL_ERR_NULL;
+    if (M > 0 && (!X || !Y)) return OBL_ERR_NULL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(y_dtype))
+      return OBL_ERR_DTYPE;
+    if (!linear_dtypes_ok(x_dtype, scale_dtype, y_dtype)) return OBL_ERR_DTYPE;
+    const int xs = elem_size(x_dtype), ss = elem_size(scale_dtype), ys = elem_size(y_dtype);
+    int64_t xb = checked_bytes(M, K, xs), wb = checked_bytes(N, K / 32, 4);
+    int64_t ab = checked_bytes(N, 1, ss), bb = checked_bytes(K, 1, ss);
+    int64_t yb = checked_bytes(M, N, ys);
+    if (xb < 0 || wb < 0 || ab < 0 || bb < 0 || yb < 0) return OBL_ERR_SHAPE;
+    if ((M > 0 && !aligned(X, xs)) || !aligned(W_packed, 4) || !aligned(a, ss) ||
+        !aligned(b, ss) || (M > 0 && !aligned(Y, ys)))
+      return OBL_ERR_ALIGN;
+    Range ry = range_of(Y, yb);
+    if (overlap(ry, range_of(X, xb)) || overlap(ry, range_of(W_packed, wb)) ||
+        overlap(ry, range_of(a, ab)) || overlap(ry, range_of(b, bb)))
+      return OBL_ERR_ALIAS;
+    obl_status st = OBL_OK;
+    Path path = choose_path(M, &st);
+    if (st != OBL_OK) return st;
+    if (M == 0) return OBL_OK;
+    LinearArgs la{X, x_dtype, M, K, W_packed, N, b, a, scale_dtype, Y, y_dtype, (hipStream_t)stream};
+    return run_linear(la, path);
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
+obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                      const uint32_t* S2_packed, int64_t Kmid,
+                      const uint32_t* S1_packed, int64_t N,
+                      const void* b, const void* m, const void* a, obl_dtype scale_dtype,
+                      float* workspace, void* Y, obl_dtype y_dtype, void* stream) {
+  try {
+    if (M < 0 || K < 1 || Kmid < 1 || N < 1 || K % 32 != 0 || Kmid % 32 != 0) return OBL_ERR_SHAPE;
+    if (!S2_packed || !S1_packed || !b || !m || !a) return OBL_ERR_NULL;
+    if (M > 0 && (!X || !Y || !workspace)) return OBL_ERR_NULL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(y_dtype))
+      return OBL_ERR_DTYPE;
+    if (!linear_dtypes_ok(x_dtype, scale_dtype, y_dtype)) return OBL_ERR_DTYPE;
+    const int xs = elem_size(x_dtype), ss = elem_size(scale_dtype), ys = elem_size(y_dtype);
+    int64_t xb = checked_bytes(M, K, xs);
+    int64_t s2b = checked_bytes(Kmid, K / 32, 4), s1b = checked_bytes(N, Kmid / 32, 4);
+    int64_t bb = checked_bytes(K, 1, ss), mb = checked_bytes(Kmid, 1, ss), ab = checked_bytes(N, 1, ss);
+    int64_t wsb = checked_bytes(M, Kmid, 4), yb = checked_bytes(M, N, ys);
+    if (xb < 0 || s2b < 0 || s1b < 0 || bb < 0 || mb < 0 || ab < 0 || wsb < 0 || yb < 0)
+      return OBL_ERR_SHAPE;
+    if ((M > 0 && !aligned(X, xs)) || !aligned(S2_packed, 4) || !aligned(S1_packed, 4) ||
+        !aligned(b, ss) || !aligned(m, ss) || !aligned(a, ss) ||
+        (M > 0 && (!aligned(workspace, 4) || !aligned(Y, ys))))
+      return OBL_ERR_ALIGN;
+    const Range ins[6] = {range_of(X, xb), range_of(S2_packed, s2b), range_of(S1_packed, s1b),
+                          range_of(b, bb), range_of(m, mb), range_of(a, ab)};
+    Range ry = range_of(Y, yb), rw = range_of(workspace, wsb);
+    for (const Range& r : ins)
+      if (overlap(ry, r) || overlap(rw, r)) return OBL_ERR_ALIAS;
+    if (overlap(ry, rw)) return OBL_ERR_ALIAS;
+    obl_status st = OBL_OK;
+    Path path = choose_path(M, &st);
+    if (st != OBL_OK) return st;
+    if (M == 0) return OBL_OK;
+    // Stage 1: T1 = ((X ⊙ b) S2^T) ⊙ m, kept in fp32 in the workspace.
+    LinearArgs s1{X, x_dtype, M, K, S2_packed, Kmid, b, m, scale_dtype, workspace, OBL_F32,
+                  (hipStream_t)stream};
+    st = run_linear(s1, path);
+    if (st != OBL_OK) return st;
+    // Stage 2: Y = (T1 S1^T) ⊙ a (no input-side scale).
+    LinearArgs s2{workspace, OBL_F32, M, Kmid, S1_packed, N, nullptr, a, scale_dtype, Y, y_dtype,
+                  (hipStream_t)stream};
+    return run_linear(s2, path);
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Shared device helpers for the libobl kernels (gfx950 / CDNA4, wave64).
+//
+// Packed sign format: uint32 P[rows][K/32]; bit j of P[r][w] is the sign of
+// column 32*w + j, 1 = -1.  A set bit is therefore exactly the IEEE sign bit
+// that has to be applied to the matching input value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace obl {
+
+enum Dtype : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Storage types.  bf16 and fp16 are carried as raw 16-bit patterns so that no
+// host-side half/bfloat class is needed in kernel signatures.
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(uint32_t(v.bits) << 16); }
+__device__ __forceinline__ float to_f32(f16_t v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, v.bits));
+}
+
+// fp32 -> bf16, round to nearest even (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ float bf16_round(float f) {
+  return __uint_as_float(bf16_bits_rne(f) << 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  static __device__ __forceinline__ void put(float* p, float v) { *p = v; }
+};
+template <> struct Store<bf16_t> {
+  static __device__ __forceinline__ void put(bf16_t* p, float v) {
+    p->bits = static_cast<uint16_t>(bf16_bits_rne(v));
+  }
+};
+
+// One 16x16x32 bf16 MFMA step with fp32 accumulation.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Operand order inside one 32-wide k-step ("pair order").
+//
+// A lane of a 16x16x32 MFMA holds 8 bf16 values of one row (A) or one column
+// (B), for lane group g = lane / 16.  Which eight of the 32 k-values a lane
+// holds is free as long as A and B agree, so the kernels use the order that
+// makes sign expansion cheapest: dword j (j = 0..3) of lane group g holds
+//     low half  <- k = 4g + j
+//     high half <- k = 4g + j + 16.
+// Shifting the sign word right by 4g and then left by (15 - j) puts the sign
+// bits of both k-values at bit 15 and bit 31, the sign bits of the two bf16
+// halves -- one shift and one bitwise op per two weights.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 expand_signs_pm1(uint32_t w_shifted) {
+  u32x4 r;
+  r.x = ((w_shifted << 15) & 0x80008000u) ^ 0x3F803F80u;  // +-1.0 bf16 pairs
+  r.y = ((w_shifted << 14) & 0x80008000u) ^ 0x3F803F80u;
+  r.z = ((w_shifted << 13) & 0x80008000u) ^ 0x3F803F80u;
+  r.w = ((w_shifted << 12) & 0x80008000u) ^ 0x3F803F80u;
+  return r;
+}
+
+// Same, but the magnitudes come from `mag` (bf16 pairs in pair order): each
+// half gets its sign flipped where the weight is -1 (v_bitop3: (x & m) ^ c).
+__device__ __forceinline__ u32x4 expand_signs_scaled(uint32_t w_shifted, u32x4 mag) {
+  u32x4 r;
+  r.x = ((w_shifted << 15) & 0x80008000u) ^ mag.x;
+  r.y = ((w_shifted << 14) & 0x80008000u) ^ mag.y;
+  r.z = ((w_shifted << 13) & 0x80008000u) ^ mag.z;
+  r.w = ((w_shifted << 12) & 0x80008000u) ^ mag.w;
+  return r;
+}
+
+// Pack two fp32 values (already representable in bf16) into one dword.
+__device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
+  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+}
+
+// Exact three-way split of an fp32 value into bf16 terms: v = hi + mid + lo
+// whenever v has at most 24 significant bits and no term underflows.  Each
+// remainder is exact in fp32 because it is the rounding error of the previous
+// bf16 rounding.
+struct Split3 { float hi, mid, lo; };
+__device__ __forceinline__ Split3 split3(float v) {
+  Split3 s;
+  s.hi = bf16_round(v);
+  float r = v - s.hi;
+  s.mid = bf16_round(r);
+  s.lo = bf16_round(r - s.mid);
+  return s;
+}
+
+}  // namespace obl

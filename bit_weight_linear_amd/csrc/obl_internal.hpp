@@ -1,0 +1,50 @@
+// Internal launcher interface between the C ABI (obl_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace obl {
+
+// One sign-binarised contraction Y = ((X ⊙ pre) · W^T) ⊙ post.
+struct LinearArgs {
+  const void* X;      // [M][K], x_dtype
+  int x_dtype;        // DT_F32 or DT_BF16
+  int64_t M, K;
+  const uint32_t* W;  // [N][K/32] packed signs
+  int64_t N;
+  const void* pre;    // [K] or nullptr (= all ones)
+  const void* post;   // [N]
+  int scale_dtype;    // DT_F32 or DT_F16
+  void* Y;            // [M][N]
+  int y_dtype;        // DT_F32 or DT_BF16
+  hipStream_t stream;
+};
+
+struct DeviceInfo {
+  int device;
+  int num_cus;
+};
+
+// Per-device scratch for split-K partial sums and tile counters.
+struct Scratch {
+  float* partials;
+  size_t partial_floats;
+  unsigned* counters;
+  size_t n_counters;
+};
+
+hipError_t device_info(DeviceInfo* out);
+hipError_t scratch_reserve(int device, size_t partial_floats, size_t n_counters, Scratch* out);
+
+hipError_t launch_pack_signs(const void* S, int s_dtype, int64_t rows, int64_t K, uint32_t* P,
+                             hipStream_t stream);
+hipError_t launch_gemv_lut(const LinearArgs& a, const DeviceInfo& dev);
+hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
+hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
+
+// Largest M served by the LUT GEMV and by the decode kernel.
+constexpr int64_t kLutMaxM = 2;
+constexpr int64_t kDecodeMaxM = 16;
+
+}  // namespace obl

@@ -1,0 +1,136 @@
+/*
+ * obl.h -- C ABI of libobl, the MI355X (gfx950) library for sign-binarised
+ * linear layers.
+ *
+ * Sources:
+ *  - OneBit page, "1bit量化" (blog.zerodtree.com): proposition 1 and its proof
+ *    (X W^T = [(X ⊙ b^T) W_sign^T] ⊙ a^T with W = W_sign ⊙ a b^T), and the
+ *    layer block under "知识蒸馏" (Y = [(X ⊙ g) W_±1^T] ⊙ h, g = b^T, h = a^T).
+ *  - DBF page, "Addition is almost all you need: Compressing large language
+ *    models with double binary factorization" (gist.science summary),
+ *    "Methodologie": W ≈ (a ⊙ A_±1 ⊙ m^T)(B_±1 ⊙ b^T), inference chain
+ *    ((((X ⊙ b^T) B_±1^T) ⊙ m^T) A_±1^T) ⊙ a^T, scale vectors in FP16.
+ *
+ * Conventions shared by every call
+ *  - All matrices are dense, row-major and contiguous.  X is [M][K]; a sign
+ *    matrix is [rows][K] with rows = outputs (the OneBit page writes X W^T
+ *    with W indexed [output][input]).
+ *  - Packed signs: uint32 P[rows][K/32].  Bit j (LSB = 0) of P[r][w] holds the
+ *    sign of column 32*w + j; 1 means -1 and 0 means +1.
+ *  - Pointers to tensors are DEVICE pointers (HIP device memory of the current
+ *    device).  `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Every call is asynchronous on `stream`: it returns once the work
+ *    is enqueued, and buffers must stay alive until that work completes.
+ *  - Ownership: the caller owns every buffer.  The library keeps no pointer
+ *    to caller memory after a call returns.  For its own split-K partial sums
+ *    it keeps one scratch buffer per device (allocated on the first call that
+ *    needs it, grown when a larger one is needed, held until process exit);
+ *    calls that overlap in time on one device (several streams or host
+ *    threads) must not both use it -- serialise them.
+ *  - Errors: every argument is validated BEFORE any HIP call; a failed check
+ *    returns its status and enqueues nothing.  No call aborts or throws across
+ *    the ABI.  HIP failures (including launch failures seen through
+ *    hipGetLastError) return OBL_ERR_HIP.
+ *  - M = 0 is a valid no-op.  N, K, Kmid, rows must be >= 1 and K, Kmid must
+ *    be multiples of 32 (the packed word width); a call that violates this
+ *    returns OBL_ERR_SHAPE.  Dimensions must also keep every byte size below
+ *    2^62.
+ */
+#ifndef OBL_H_
+#define OBL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OBL_OK = 0,
+  OBL_ERR_NULL = 1,     /* a required pointer is NULL */
+  OBL_ERR_SHAPE = 2,    /* a dimension is negative / zero where not allowed / not a multiple of 32 */
+  OBL_ERR_DTYPE = 3,    /* unsupported dtype or dtype combination */
+  OBL_ERR_ALIGN = 4,    /* a pointer is not aligned to its element size (packed words: 4 bytes) */
+  OBL_ERR_ALIAS = 5,    /* an output overlaps an input or another output */
+  OBL_ERR_HIP = 6,      /* the HIP runtime reported an error */
+  OBL_ERR_INTERNAL = 7  /* unexpected internal failure */
+} obl_status;
+
+typedef enum {
+  OBL_F32 = 0,
+  OBL_F16 = 1,
+  OBL_BF16 = 2,
+  OBL_I8 = 3
+} obl_dtype;
+
+/*
+ * obl_pack_signs -- W_sign = Sign(S) bit-packed along K.
+ *   OneBit page, "rank-1 approximation" block: W = W_sign ⊙ |W| with
+ *   W_sign = Sign(W).  Sign of zero is not given there; a value packs as -1
+ *   exactly when it compares below zero (so 0, -0.0 and NaN pack as +1).
+ *
+ *   S       [rows][K] of s_dtype (OBL_I8, OBL_F32, OBL_F16 or OBL_BF16), device.
+ *   packed  [rows][K/32] uint32, device, written.  Must not overlap S.
+ *   Errors: OBL_ERR_NULL, OBL_ERR_SHAPE (rows < 1, K < 1 or K % 32 != 0),
+ *           OBL_ERR_DTYPE, OBL_ERR_ALIGN (S not aligned to its element, packed
+ *           not 4-byte aligned), OBL_ERR_ALIAS, OBL_ERR_HIP.
+ */
+obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_t K,
+                          uint32_t* packed, void* stream);
+
+/*
+ * obl_linear -- Y[M][N] = ((X[M][K] ⊙ b[K]) · W_sign[N][K]^T) ⊙ a[N].
+ *   OneBit page, proposition 1 (right-hand side) and the layer block under
+ *   "知识蒸馏" (b is the layer's g, a its h).
+ *
+ *   X         [M][K], x_dtype OBL_F32 or OBL_BF16.
+ *   W_packed  [N][K/32] packed signs (format above).
+ *   a         [N], b [K], both scale_dtype (OBL_F32 or OBL_F16).
+ *   Y         [M][N], y_dtype OBL_F32 or OBL_BF16, written; must not overlap
+ *             any input.
+ *   Arithmetic: for M <= 16 (decode) x·b is formed in fp32 and the contraction
+ *   keeps fp32 accuracy (|Y - Y_exact| <= 1e-5 · |a_j| Σ_k |x_ik b_k| before the
+ *   final cast); for M > 16 (prefill) the contraction runs on bf16 matrix
+ *   cores with one bf16 rounding of the input-side operand and fp32
+ *   accumulation (<= 8e-3 on the same scale, including a bf16 output cast).
+ *   Errors: OBL_ERR_NULL, OBL_ERR_SHAPE, OBL_ERR_DTYPE, OBL_ERR_ALIGN,
+ *           OBL_ERR_ALIAS, OBL_ERR_HIP.
+ */
+obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                      const uint32_t* W_packed, int64_t N,
+                      const void* a, const void* b, obl_dtype scale_dtype,
+                      void* Y, obl_dtype y_dtype, void* stream);
+
+/*
+ * dbf_linear -- Y[M][N] = ((((X ⊙ b) · S2[Kmid][K]^T) ⊙ m) · S1[N][Kmid]^T) ⊙ a.
+ *   DBF page, "Methodologie": inference chain with S2 = B_±1, S1 = A_±1.
+ *
+ *   X          [M][K], x_dtype OBL_F32 or OBL_BF16.
+ *   S2_packed  [Kmid][K/32], S1_packed [N][Kmid/32] packed signs.
+ *   b [K], m [Kmid], a [N], all scale_dtype (OBL_F32 or OBL_F16).
+ *   workspace  float32 [M][Kmid], caller-owned.  When the call's work has
+ *              completed it holds T1 = ((X ⊙ b) S2^T) ⊙ m (stage 1, kept in
+ *              fp32); stage 2 reads it.  Must not overlap any other argument.
+ *   Y          [M][N], y_dtype OBL_F32 or OBL_BF16.
+ *   Arithmetic: each stage follows obl_linear's rules for the same M
+ *   (stage 2 has no input-side scale).
+ *   Errors: as obl_linear.
+ */
+obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                      const uint32_t* S2_packed, int64_t Kmid,
+                      const uint32_t* S1_packed, int64_t N,
+                      const void* b, const void* m, const void* a, obl_dtype scale_dtype,
+                      float* workspace, void* Y, obl_dtype y_dtype, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* obl_status_string(obl_status status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int obl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OBL_H_ */

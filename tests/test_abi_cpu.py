@@ -1,0 +1,137 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching HIP (so these run without a GPU).
+
+Pointers here are fake addresses: every call below fails validation (or is the
+M = 0 no-op) before any HIP call, so nothing is dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "obl.h")
+
+b = pytest.importorskip("bit_weight_linear_amd.binding", reason="libobl.so not built")
+L = b.lib
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(obl_\w+|dbf_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("obl_pack_signs", "obl_linear", "dbf_linear"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported"
+    assert set(declared_functions()) == set(b.EXPORTS)
+
+
+def test_status_strings_and_version():
+    for code in range(8):
+        assert L.obl_status_string(code)
+    assert L.obl_status_string(99) == b"OBL_ERR_UNKNOWN"
+    assert L.obl_version() >= 100
+
+
+# Fake but aligned, non-overlapping device addresses.
+X, W, A, B_, Y, WS, S1 = (P(0x10_0000_0000 * (i + 1)) for i in range(7))
+
+
+def lin(X=X, xd=b.OBL_BF16, M=1, K=4096, W=W, N=11008, a=A, bb=B_, sd=b.OBL_F16, Y=Y, yd=b.OBL_F32):
+    return L.obl_linear(X, xd, M, K, W, N, a, bb, sd, Y, yd, None)
+
+
+def test_linear_valid_m0_is_noop():
+    assert lin(M=0) == b.OBL_OK
+    assert lin(M=0, X=None, Y=None) == b.OBL_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), b.OBL_ERR_NULL),
+    (dict(a=None), b.OBL_ERR_NULL),
+    (dict(bb=None), b.OBL_ERR_NULL),
+    (dict(X=None), b.OBL_ERR_NULL),
+    (dict(Y=None), b.OBL_ERR_NULL),
+    (dict(M=-1), b.OBL_ERR_SHAPE),
+    (dict(K=0), b.OBL_ERR_SHAPE),
+    (dict(K=100), b.OBL_ERR_SHAPE),
+    (dict(N=0), b.OBL_ERR_SHAPE),
+    (dict(M=1 << 40, K=1 << 30), b.OBL_ERR_SHAPE),
+    (dict(xd=b.OBL_I8), b.OBL_ERR_DTYPE),
+    (dict(xd=b.OBL_F16), b.OBL_ERR_DTYPE),
+    (dict(sd=b.OBL_BF16), b.OBL_ERR_DTYPE),
+    (dict(yd=b.OBL_F16), b.OBL_ERR_DTYPE),
+    (dict(yd=7), b.OBL_ERR_DTYPE),
+    (dict(X=P(0x10_0000_0001)), b.OBL_ERR_ALIGN),
+    (dict(W=P(0x20_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(Y=P(0x50_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(Y=P(0x10_0000_0000 + 4096)), b.OBL_ERR_ALIAS),      # Y inside X
+    (dict(Y=P(0x20_0000_0000 + 1024)), b.OBL_ERR_ALIAS),      # Y inside W
+    (dict(a=P(0x50_0000_0000 + 8)), b.OBL_ERR_ALIAS),         # a inside Y
+])
+def test_linear_rejects(kw, code):
+    assert lin(**kw) == code
+
+
+def test_forced_path_must_fit_m(monkeypatch):
+    monkeypatch.setenv("OBL_PATH", "lut")
+    assert lin(M=3) == b.OBL_ERR_SHAPE
+    monkeypatch.setenv("OBL_PATH", "decode")
+    assert lin(M=17) == b.OBL_ERR_SHAPE
+    assert lin(M=0) == b.OBL_OK
+
+
+def dbf(X=X, M=8, K=4096, S2=W, Kmid=3072, S1_=S1, N=4096, bb=B_, m=A, a=P(0x80_0000_0000),
+        sd=b.OBL_F16, ws=WS, Y=Y, yd=b.OBL_F32, xd=b.OBL_BF16):
+    return L.dbf_linear(X, xd, M, K, S2, Kmid, S1_, N, bb, m, a, sd, ws, Y, yd, None)
+
+
+def test_dbf_m0_noop():
+    assert dbf(M=0) == b.OBL_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S2=None), b.OBL_ERR_NULL),
+    (dict(S1_=None), b.OBL_ERR_NULL),
+    (dict(m=None), b.OBL_ERR_NULL),
+    (dict(ws=None), b.OBL_ERR_NULL),
+    (dict(Kmid=100), b.OBL_ERR_SHAPE),
+    (dict(Kmid=0), b.OBL_ERR_SHAPE),
+    (dict(K=48), b.OBL_ERR_SHAPE),
+    (dict(sd=b.OBL_I8), b.OBL_ERR_DTYPE),
+    (dict(ws=P(0x60_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(ws=P(0x10_0000_0000 + 64)), b.OBL_ERR_ALIAS),        # workspace inside X
+    (dict(ws=P(0x50_0000_0000)), b.OBL_ERR_ALIAS),             # workspace == Y
+    (dict(Y=P(0x30_0000_0000 + 4)), b.OBL_ERR_ALIAS),          # Y inside a
+])
+def test_dbf_rejects(kw, code):
+    assert dbf(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, b.OBL_I8, 4, 64, W), b.OBL_ERR_NULL),
+    ((X, b.OBL_I8, 4, 64, None), b.OBL_ERR_NULL),
+    ((X, b.OBL_I8, 0, 64, W), b.OBL_ERR_SHAPE),
+    ((X, b.OBL_I8, 4, 48, W), b.OBL_ERR_SHAPE),
+    ((X, 9, 4, 64, W), b.OBL_ERR_DTYPE),
+    ((P(0x10_0000_0002), b.OBL_F32, 4, 64, W), b.OBL_ERR_ALIGN),
+    ((X, b.OBL_I8, 4, 64, P(0x10_0000_0000 + 32)), b.OBL_ERR_ALIAS),
+])
+def test_pack_rejects(args, code):
+    assert L.obl_pack_signs(*args, None) == code
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        b.pack_signs(torch.ones((2, 32), dtype=torch.int8))
