@@ -59,19 +59,29 @@ __device__ __forceinline__ u32x4 interleave_pairs(u32x2 r0, u32x2 r1) {
   return o;
 }
 
+// One pipeline stage of global data held in registers between its loads and
+// its LDS store.  Loads are issued without branches (an invalid element reads a
+// clamped, valid address and is zeroed at store time), so a stage costs one
+// memory round trip and overlaps the MFMA work of the previous stage.  In raw
+// mode the registers hold the loaded bits untouched and the pair-order
+// interleave happens at store time; convert mode (fp32 or misaligned X) does
+// its arithmetic at load time.
 template <int AMODE, typename XT, typename ST, bool PRE>
 struct Stager {
-  // Registers holding one stage of global data before it is written to LDS.
-  u32x4 a[GM_SLOTS_PER_THREAD];
+  static constexpr bool kRaw = AMODE == A_RAW;
+  static constexpr bool kMag = kRaw && PRE;
+  u32x2 r0[GM_SLOTS_PER_THREAD], r1[GM_SLOTS_PER_THREAD];  // raw mode
+  u32x4 cv[GM_SLOTS_PER_THREAD];                           // convert mode
+  uint32_t valid;                                          // bit i: slot i in range
   uint32_t bw;
-  u32x4 mag;
+  u32x2 p0, p1;                                            // raw fp16/f32 b words (mag)
 
   __device__ __forceinline__ void load(const XT* __restrict__ X, int64_t M, int64_t K,
                                        const uint32_t* __restrict__ W, int64_t N,
                                        const ST* __restrict__ pre, int64_t m0, int64_t n0,
                                        int64_t kt, int tid) {
     const int64_t kw = K >> 5;
-    // A slots: slot = tid + 512 i -> (t, row, g) with g fastest.
+    valid = 0;
 #pragma unroll
     for (int i = 0; i < GM_SLOTS_PER_THREAD; ++i) {
       const int slot = tid + GM_THREADS * i;
@@ -80,68 +90,103 @@ struct Stager {
       const int t = slot >> 10;
       const int64_t gr = m0 + row;
       const int64_t step = kt * GM_STEPS + t;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (gr < M && step < kw) {
-        const int64_t kb = step * 32 + 4 * g;
-        const XT* xr = X + gr * K + kb;
-        if constexpr (AMODE == A_RAW) {
-          const u32x2 r0 = *reinterpret_cast<const u32x2*>(xr);
-          const u32x2 r1 = *reinterpret_cast<const u32x2*>(xr + 16);
-          v = interleave_pairs(r0, r1);
-        } else {
-          uint32_t d[4];
+      const bool ok = gr < M && step < kw;
+      valid |= uint32_t(ok) << i;
+      const int64_t kb = step * 32 + 4 * g;
+      const XT* xr = X + (ok ? gr * K + kb : 0);
+      if constexpr (kRaw) {
+        r0[i] = *reinterpret_cast<const u32x2*>(xr);
+        r1[i] = *reinterpret_cast<const u32x2*>(xr + 16);
+      } else {
+        float lo[4], hi[4], plo[4], phi[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float lo = to_f32(xr[j]), hi = to_f32(xr[j + 16]);
-            if (PRE) {
-              lo *= to_f32(pre[kb + j]);
-              hi *= to_f32(pre[kb + j + 16]);
-            }
-            d[j] = pack_bf16_pair(lo, hi);
+        for (int j = 0; j < 4; ++j) {
+          lo[j] = to_f32(xr[j]);
+          hi[j] = to_f32(xr[j + 16]);
+          plo[j] = 1.f;
+          phi[j] = 1.f;
+          if constexpr (PRE) {
+            const ST* pr = pre + (ok ? kb : 0);
+            plo[j] = to_f32(pr[j]);
+            phi[j] = to_f32(pr[j + 16]);
           }
-          v = u32x4{d[0], d[1], d[2], d[3]};
         }
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = ok ? pack_bf16_pair(lo[j] * plo[j], hi[j] * phi[j]) : 0u;
+        cv[i] = u32x4{d[0], d[1], d[2], d[3]};
       }
-      a[i] = v;
     }
     // Sign words: thread -> (column, step).
-    bw = 0u;
-    if (tid < GM_BN * GM_STEPS) {
+    {
       const int c = tid >> 1, t = tid & 1;
       const int64_t n = n0 + c, step = kt * GM_STEPS + t;
-      if (n < N && step < kw) bw = W[n * kw + step];
+      const bool ok = tid < GM_BN * GM_STEPS && n < N && step < kw;
+      bw = W[ok ? n * kw + step : 0];   // masked at store time
+      valid |= uint32_t(ok) << 8;
     }
-    // Magnitudes of B in raw mode: bf16(b) pairs per (step, lane group).
-    if constexpr (AMODE == A_RAW && PRE) {
+    // Raw b for the magnitudes of B in raw mode: bf16(b) pairs per (step, group).
+    if constexpr (kMag) {
       const int r = tid - GM_BN * GM_STEPS;
-      mag = u32x4{0u, 0u, 0u, 0u};
-      if (r >= 0 && r < GM_STEPS * 4) {
-        const int t = r >> 2, g = r & 3;
-        const int64_t step = kt * GM_STEPS + t;
-        if (step < kw) {
-          const int64_t kb = step * 32 + 4 * g;
-          uint32_t d[4];
+      const int t = (r >> 2) & 1, g = r & 3;
+      const int64_t step = kt * GM_STEPS + t;
+      const bool ok = r >= 0 && r < GM_STEPS * 4 && step < kw;
+      valid |= uint32_t(ok) << 9;
+      const ST* pr = pre + (ok ? step * 32 + 4 * g : 0);
+      if constexpr (sizeof(ST) == 2) {
+        p0 = *reinterpret_cast<const u32x2*>(pr);
+        p1 = *reinterpret_cast<const u32x2*>(pr + 16);
+      } else {
+        // fp32 b: round to bf16 here (small: 8 threads, 8 values each).
+        uint32_t d[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) d[j] = pack_bf16_pair(to_f32(pre[kb + j]), to_f32(pre[kb + j + 16]));
-          mag = u32x4{d[0], d[1], d[2], d[3]};
-        }
+        for (int j = 0; j < 4; ++j) d[j] = pack_bf16_pair(to_f32(pr[j]), to_f32(pr[j + 16]));
+        p0 = u32x2{d[0], d[1]};
+        p1 = u32x2{d[2], d[3]};
       }
     }
   }
 
   __device__ __forceinline__ void store(GemmSmem& sm, int buf, int tid) const {
+    // Every thread consumes every staged register here, including the ones
+    // only some threads write to LDS: otherwise the next stage's loads into
+    // the same registers would wait for this stage's loads to land.
+    if constexpr (kMag) asm volatile("" ::"v"(bw), "v"(p0), "v"(p1));
+    else asm volatile("" ::"v"(bw));
 #pragma unroll
     for (int i = 0; i < GM_SLOTS_PER_THREAD; ++i) {
       const int slot = tid + GM_THREADS * i;
       const int g = slot & 3;
       const int row = (slot >> 2) & (GM_BM - 1);
       const int t = slot >> 10;
-      sm.a[buf][t][row >> 4][16 * g + (row & 15)] = a[i];
+      u32x4 v;
+      if constexpr (kRaw) v = interleave_pairs(r0[i], r1[i]);
+      else v = cv[i];
+      if (!((valid >> i) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
+      sm.a[buf][t][row >> 4][16 * g + (row & 15)] = v;
     }
-    if (tid < GM_BN * GM_STEPS) sm.bw[buf][tid >> 1][tid & 1] = bw;
-    if (AMODE == A_RAW && PRE) {
+    if (tid < GM_BN * GM_STEPS) sm.bw[buf][tid >> 1][tid & 1] = ((valid >> 8) & 1u) ? bw : 0u;
+    if constexpr (kMag) {
       const int r = tid - GM_BN * GM_STEPS;
-      if (r >= 0 && r < GM_STEPS * 4) sm.mag[buf][r >> 2][r & 3] = mag;
+      if (r >= 0 && r < GM_STEPS * 4) {
+        u32x4 m;
+        if constexpr (sizeof(ST) == 2) {
+          // fp16 (b_j, b_{j+16}) -> bf16 pairs in pair order.
+          const uint32_t lo[2] = {p0.x, p0.y}, hi[2] = {p1.x, p1.y};
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint16_t bl = uint16_t(lo[j >> 1] >> (16 * (j & 1)));
+            const uint16_t bh = uint16_t(hi[j >> 1] >> (16 * (j & 1)));
+            d[j] = pack_bf16_pair(to_f32(f16_t{bl}), to_f32(f16_t{bh}));
+          }
+          m = u32x4{d[0], d[1], d[2], d[3]};
+        } else {
+          m = u32x4{p0.x, p0.y, p1.x, p1.y};
+        }
+        if (!((valid >> 9) & 1u)) m = u32x4{0u, 0u, 0u, 0u};
+        sm.mag[buf][r >> 2][r & 3] = m;
+      }
     }
   }
 };
@@ -176,6 +221,14 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < GM_FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Output scales of this lane's columns, fetched before the main loop.
+  float post_c[GM_FN];
+#pragma unroll
+  for (int j = 0; j < GM_FN; ++j) {
+    const int64_t n = n0 + wn * (GM_FN * 16) + j * 16 + (lane & 15);
+    post_c[j] = to_f32(post[n < N ? n : N - 1]);
+  }
+
   Stager<AMODE, XT, ST, PRE> st;
   st.load(X, M, K, W, N, pre, m0, n0, 0, tid);
   st.store(sm, 0, tid);
@@ -208,7 +261,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(
   for (int j = 0; j < GM_FN; ++j) {
     const int64_t n = n0 + wn * (GM_FN * 16) + j * 16 + (lane & 15);
     if (n >= N) continue;
-    const float s = to_f32(post[n]);
+    const float s = post_c[j];
 #pragma unroll
     for (int i = 0; i < GM_FM; ++i) {
 #pragma unroll

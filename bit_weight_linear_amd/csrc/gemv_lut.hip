@@ -67,50 +67,68 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
   const int64_t kw = K >> 5;
 
   float acc[LUT_RPH][MR];
+  float post_r[LUT_RPH];  // output scales of this half-wave's rows, fetched up front
 #pragma unroll
-  for (int r = 0; r < LUT_RPH; ++r)
+  for (int r = 0; r < LUT_RPH; ++r) {
+    const int row = hw + LUT_HALFWAVES * r;
+    post_r[r] = to_f32(post[row0 + (row < nrows ? row : nrows - 1)]);
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+  }
 
   for (int64_t s0 = 0; s0 < K; s0 += LUT_SLAB_K) {
+    // All global loads of the slab are issued first and without branches
+    // (clamped addresses, masked afterwards), so each thread pays one memory
+    // round trip.  Table inputs go first: the build waits only for them while
+    // the sign words are still in flight.
+    const int g = tid;                       // this thread's table group
+    const int64_t k = s0 + 4 * g;
+    const bool kval = k < K;                 // K % 32 == 0: a group is all in or all out
+    const int64_t kk = kval ? k : 0;
+    float xr[MR][4], pr[4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[m][i] = to_f32(X[m * K + kk + i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (PRE) pr[i] = to_f32(pre[kk + i]);
+      else pr[i] = 1.f;
+    }
+
     // 1. Sign words of this lane's chunk for each of its rows.
     const int64_t w0 = (s0 >> 5) + 4 * c;
     u32x4 wv[LUT_RPH];
 #pragma unroll
     for (int r = 0; r < LUT_RPH; ++r) {
       const int row = hw + LUT_HALFWAVES * r;
-      wv[r] = u32x4{0u, 0u, 0u, 0u};
-      if (row < nrows) {
-        const uint32_t* src = W + (row0 + row) * kw + w0;
-        if (VEC4) {
-          if (w0 < kw) wv[r] = *reinterpret_cast<const u32x4*>(src);
-        } else {
-          if (w0 + 0 < kw) wv[r].x = src[0];
-          if (w0 + 1 < kw) wv[r].y = src[1];
-          if (w0 + 2 < kw) wv[r].z = src[2];
-          if (w0 + 3 < kw) wv[r].w = src[3];
+      const int64_t rr = row0 + (row < nrows ? row : nrows - 1);
+      const uint32_t* src = W + rr * kw;
+      if (VEC4) {
+        const bool ok = row < nrows && w0 < kw;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + (w0 < kw ? w0 : kw - 4));
+        wv[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        uint32_t t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = row < nrows && w0 + i < kw;
+          const uint32_t v = src[w0 + i < kw ? w0 + i : kw - 1];
+          t[i] = ok ? v : 0u;
         }
+        wv[r] = u32x4{t[0], t[1], t[2], t[3]};
       }
     }
 
-    // 2. Table for this slab.  Thread tid owns group g = tid (k = s0 + 4g ..).
+    // 2. Table for this slab.  Thread tid owns group g (k = s0 + 4g .. +3).
     if (s0 > 0) __syncthreads();  // the previous slab's lookups are done
     {
-      const int g = tid;
-      const int64_t k = s0 + 4 * g;
       const int col = 33 * (g >> 5) + (g & 31);
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         float x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = 0.f;
-          if (k + i < K) {
-            v = to_f32(X[m * K + k + i]);
-            if (PRE) v *= to_f32(pre[k + i]);
-          }
-          x[i] = v;
-        }
+        for (int i = 0; i < 4; ++i) x[i] = kval ? xr[m][i] * pr[i] : 0.f;
         // bit i of the nibble set -> -x_i.  p indexed by bits (0,1), q by bits (2,3).
         const float p0 = x[0] + x[1], p2 = x[0] - x[1];
         const float q0 = x[2] + x[3], q2 = x[2] - x[3];
@@ -148,9 +166,8 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
     for (int m = 0; m < MR; ++m) tot[m] = halfwave_sum(acc[r][m]);
     if (c == 0 && row < nrows) {
       const int64_t n = row0 + row;
-      const float s = to_f32(post[n]);
 #pragma unroll
-      for (int m = 0; m < MR; ++m) Store<YT>::put(&Y[m * N + n], tot[m] * s);
+      for (int m = 0; m < MR; ++m) Store<YT>::put(&Y[m * N + n], tot[m] * post_r[r]);
     }
   }
 }

@@ -115,36 +115,26 @@ hipError_t device_info(DeviceInfo* out) {
   return hipSuccess;
 }
 
-hipError_t scratch_reserve(int device, size_t partial_floats, size_t n_counters, Scratch* out) {
+hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out) {
   std::lock_guard<std::mutex> lk(g_mu);
   Scratch& s = g_scratch[device];
-  if (s.partial_floats >= partial_floats && s.n_counters >= n_counters) {
+  if (s.partial_floats >= partial_floats) {
     *out = s;
     return hipSuccess;
   }
-  size_t pf = partial_floats > s.partial_floats ? partial_floats : s.partial_floats;
-  size_t nc = n_counters > s.n_counters ? n_counters : s.n_counters;
-  if (pf < (size_t(8) << 20)) pf = size_t(8) << 20;  // 32 MiB of partial sums
-  if (nc < 65536) nc = 65536;
+  size_t pf = partial_floats;
+  if (pf < (size_t(8) << 20)) pf = size_t(8) << 20;  // at least 32 MiB of partial sums
   if (s.partials) {
-    // Work already enqueued may still use the old buffers.
+    // Work already enqueued may still use the old buffer.
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return e;
     (void)hipFree(s.partials);
-    (void)hipFree(s.counters);
     s = Scratch{};
   }
   float* p = nullptr;
-  unsigned* c = nullptr;
   hipError_t e = hipMalloc(&p, pf * sizeof(float));
   if (e != hipSuccess) return e;
-  e = hipMalloc(&c, nc * sizeof(unsigned));
-  if (e != hipSuccess) { (void)hipFree(p); return e; }
-  e = hipMemset(c, 0, nc * sizeof(unsigned));  // counters start (and are left) at zero
-  if (e != hipSuccess) { (void)hipFree(p); (void)hipFree(c); return e; }
-  e = hipDeviceSynchronize();
-  if (e != hipSuccess) return e;
-  s = Scratch{p, pf, c, nc};
+  s = Scratch{p, pf};
   *out = s;
   return hipSuccess;
 }

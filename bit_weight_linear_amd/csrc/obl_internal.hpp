@@ -26,16 +26,14 @@ struct DeviceInfo {
   int num_cus;
 };
 
-// Per-device scratch for split-K partial sums and tile counters.
+// Per-device scratch for split-K partial sums.
 struct Scratch {
   float* partials;
   size_t partial_floats;
-  unsigned* counters;
-  size_t n_counters;
 };
 
 hipError_t device_info(DeviceInfo* out);
-hipError_t scratch_reserve(int device, size_t partial_floats, size_t n_counters, Scratch* out);
+hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out);
 
 hipError_t launch_pack_signs(const void* S, int s_dtype, int64_t rows, int64_t K, uint32_t* P,
                              hipStream_t stream);

@@ -23,10 +23,12 @@
  *    is enqueued, and buffers must stay alive until that work completes.
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer
  *    to caller memory after a call returns.  For its own split-K partial sums
- *    it keeps one scratch buffer per device (allocated on the first call that
- *    needs it, grown when a larger one is needed, held until process exit);
- *    calls that overlap in time on one device (several streams or host
- *    threads) must not both use it -- serialise them.
+ *    (decode sizes, M <= 16) it keeps one scratch buffer per device, allocated
+ *    with hipMalloc on the first call that needs it (at least 32 MiB), grown
+ *    when a larger one is needed (after a device synchronise) and held until
+ *    process exit.  Calls that overlap in time on one device (several streams
+ *    or host threads) must not both use it -- serialise them -- and the first
+ *    such call must not be made inside HIP stream capture.
  *  - Errors: every argument is validated BEFORE any HIP call; a failed check
  *    returns its status and enqueues nothing.  No call aborts or throws across
  *    the ABI.  HIP failures (including launch failures seen through
