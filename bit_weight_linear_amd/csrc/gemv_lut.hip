@@ -16,9 +16,12 @@
 //    128 k, nibble q of that chunk -- lives in dword column 33c + q of each
 //    16-entry row, so the 32 lanes of a half-wave (c = 0..31, same q) hit 32
 //    different banks whatever nibbles they read.
-//  * Lane l of a half-wave owns chunk c = l % 32 (4 sign words, one 128-bit
-//    coalesced load per row); a half-wave walks whole rows.  The sign loads are
-//    issued before the table build so their HBM latency overlaps it.
+//  * Lane l of a half-wave owns chunk c = l % 32 (4 sign words per row); a
+//    half-wave walks whole rows.  All loads are issued up front, table inputs
+//    first: every wave issues its X/b loads, a bare barrier, then the 128-bit
+//    sign loads, so the small L2-resident inputs are not queued behind the HBM
+//    stream in the CU's memory pipeline; the table barrier waits only for LDS,
+//    so the sign loads stay in flight while the table is built.
 //  * Per-lane partial sums are reduced across the 32 lanes with DPP
 //    (quad_perm, half-mirror, mirror) plus one swizzle, in a fixed order, so
 //    results are bitwise reproducible.  No atomics.
@@ -32,8 +35,6 @@ constexpr int LUT_THREADS = 1024;
 constexpr int LUT_HALFWAVES = LUT_THREADS / 32;  // 32
 constexpr int LUT_SLAB_K = 4096;                 // 32 chunks x 128 k
 constexpr int LUT_COLS = 33 * 32;                // padded columns per nibble row
-constexpr int LUT_RPH = 4;                       // rows per half-wave (max)
-constexpr int LUT_MAX_ROWS = LUT_HALFWAVES * LUT_RPH;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -50,7 +51,7 @@ __device__ __forceinline__ float halfwave_sum(float v) {
   return v;
 }
 
-template <int MR, typename XT, typename ST, typename YT, bool PRE, bool VEC4>
+template <int MR, int RPH, bool MULTI, typename XT, typename ST, typename YT, bool PRE, bool VEC4>
 __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
     const XT* __restrict__ X, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y,
@@ -66,21 +67,24 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
   const int nrows = (int)min((int64_t)rows_per_block, N - row0);
   const int64_t kw = K >> 5;
 
-  float acc[LUT_RPH][MR];
-  float post_r[LUT_RPH];  // output scales of this half-wave's rows, fetched up front
+  float acc[RPH][MR];
+  float post_r[RPH];  // output scales of this half-wave's rows, fetched up front
 #pragma unroll
-  for (int r = 0; r < LUT_RPH; ++r) {
+  for (int r = 0; r < RPH; ++r) {
     const int row = hw + LUT_HALFWAVES * r;
     post_r[r] = to_f32(post[row0 + (row < nrows ? row : nrows - 1)]);
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
   }
 
-  for (int64_t s0 = 0; s0 < K; s0 += LUT_SLAB_K) {
-    // All global loads of the slab are issued first and without branches
-    // (clamped addresses, masked afterwards), so each thread pays one memory
-    // round trip.  Table inputs go first: the build waits only for them while
-    // the sign words are still in flight.
+  // K <= 4096 (MULTI = false) runs the slab body once, with no loop: a loop
+  // header would drain vmcnt and wait for the output-scale loads above.
+  const int64_t nslab = MULTI ? K : 1;
+  for (int64_t s0 = 0; s0 < nslab; s0 += LUT_SLAB_K) {
+    // Table inputs first, from every wave, then a barrier (no memory wait),
+    // then the sign words: the CU's memory pipeline serves requests in issue
+    // order, so the small, L2-resident table inputs are not queued behind the
+    // HBM-bound sign stream.  Loads are unconditional (clamped addresses).
     const int g = tid;                       // this thread's table group
     const int64_t k = s0 + 4 * g;
     const bool kval = k < K;                 // K % 32 == 0: a group is all in or all out
@@ -95,33 +99,31 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
       if constexpr (PRE) pr[i] = to_f32(pre[kk + i]);
       else pr[i] = 1.f;
     }
+    // Barrier without a memory wait: every wave has issued its table inputs
+    // before any wave issues sign loads, and (for later slabs) every wave has
+    // finished reading the previous table.
+    __builtin_amdgcn_s_barrier();
 
-    // 1. Sign words of this lane's chunk for each of its rows.
+    // Sign words of this lane's chunk for each of its rows.  Rows past the
+    // block's last row read a clamped row and are never looked up; words past
+    // K read a clamped address and meet zero table entries, so they add nothing.
     const int64_t w0 = (s0 >> 5) + 4 * c;
-    u32x4 wv[LUT_RPH];
+    u32x4 wv[RPH];
 #pragma unroll
-    for (int r = 0; r < LUT_RPH; ++r) {
+    for (int r = 0; r < RPH; ++r) {
       const int row = hw + LUT_HALFWAVES * r;
-      const int64_t rr = row0 + (row < nrows ? row : nrows - 1);
-      const uint32_t* src = W + rr * kw;
-      if (VEC4) {
-        const bool ok = row < nrows && w0 < kw;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + (w0 < kw ? w0 : kw - 4));
-        wv[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t* src = W + (row0 + (row < nrows ? row : nrows - 1)) * kw;
+      if constexpr (VEC4) {
+        wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (w0 < kw ? w0 : kw - 4)));
       } else {
         uint32_t t[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = row < nrows && w0 + i < kw;
-          const uint32_t v = src[w0 + i < kw ? w0 + i : kw - 1];
-          t[i] = ok ? v : 0u;
-        }
+        for (int i = 0; i < 4; ++i) t[i] = src[w0 + i < kw ? w0 + i : kw - 1];
         wv[r] = u32x4{t[0], t[1], t[2], t[3]};
       }
     }
 
-    // 2. Table for this slab.  Thread tid owns group g (k = s0 + 4g .. +3).
-    if (s0 > 0) __syncthreads();  // the previous slab's lookups are done
+    // Table for this slab.  Thread tid owns group g (k = s0 + 4g .. +3).
     {
       const int col = 33 * (g >> 5) + (g & 31);
 #pragma unroll
@@ -138,12 +140,17 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
         for (int n = 0; n < 16; ++n) lut[(n * LUT_COLS + col) * MR + m] = p[n & 3] + q[n >> 2];
       }
     }
-    __syncthreads();
+    lds_barrier();  // table visible; sign loads may still be in flight
+    // Pin every row's sign load above this point (otherwise the compiler sinks
+    // the loads of rows only some half-waves have into their conditional
+    // blocks, i.e. after the table build); the wait for the data lands here.
+#pragma unroll
+    for (int r = 0; r < RPH; ++r) asm volatile("" : "+v"(wv[r]));
 
-    // 3. Lookups: one nibble -> one signed 4-term sum per input row.
+    // Lookups: one nibble -> one signed 4-term sum per input row.
     const int cbase = 33 * c;
 #pragma unroll
-    for (int r = 0; r < LUT_RPH; ++r) {
+    for (int r = 0; r < RPH; ++r) {
       if (hw + LUT_HALFWAVES * r < nrows) {
         const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
 #pragma unroll
@@ -157,10 +164,13 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
     }
   }
 
-  // 4. Reduce across the half-wave and write the scaled outputs.
+  // Reduce across the half-wave and write the scaled outputs.  A row index is
+  // uniform within a half-wave; the reduction runs while any half of the wave
+  // still has a row (DPP reads stay inside each half).
 #pragma unroll
-  for (int r = 0; r < LUT_RPH; ++r) {
+  for (int r = 0; r < RPH; ++r) {
     const int row = hw + LUT_HALFWAVES * r;
+    if ((hw & ~1) + LUT_HALFWAVES * r >= nrows) break;   // neither half of this wave has row r
     float tot[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) tot[m] = halfwave_sum(acc[r][m]);
@@ -172,25 +182,42 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
   }
 }
 
-template <int MR, typename XT, typename ST, typename YT, bool PRE>
-hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
-  int64_t blocks = dev.num_cus;
-  int64_t rpb = (a.N + blocks - 1) / blocks;
-  if (rpb < 16) rpb = a.N < 16 ? a.N : 16;          // amortise the table over >= 16 rows
-  if (rpb > LUT_MAX_ROWS) rpb = LUT_MAX_ROWS;
-  blocks = (a.N + rpb - 1) / rpb;
+template <int MR, int RPH, typename XT, typename ST, typename YT, bool PRE>
+hipError_t launch_rph(const LinearArgs& a, int64_t blocks, int rpb) {
   const bool vec4 = (a.K % 128 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0);
   auto X = static_cast<const XT*>(a.X);
   auto pre = static_cast<const ST*>(a.pre);
   auto post = static_cast<const ST*>(a.post);
   auto Y = static_cast<YT*>(a.Y);
-  if (vec4)
-    hipLaunchKernelGGL((gemv_lut_kernel<MR, XT, ST, YT, PRE, true>), dim3((unsigned)blocks),
-                       dim3(LUT_THREADS), 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, (int)rpb);
+  const dim3 grid((unsigned)blocks), block(LUT_THREADS);
+  const bool multi = a.K > LUT_SLAB_K;
+  if (vec4 && !multi)
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, false, XT, ST, YT, PRE, true>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb);
+  else if (vec4)
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, true, XT, ST, YT, PRE, true>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb);
   else
-    hipLaunchKernelGGL((gemv_lut_kernel<MR, XT, ST, YT, PRE, false>), dim3((unsigned)blocks),
-                       dim3(LUT_THREADS), 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, (int)rpb);
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, true, XT, ST, YT, PRE, false>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb);
   return hipGetLastError();
+}
+
+// Rows per block: about N / #CUs (one block per CU), at least 16 to amortise
+// the table build, at most 32 x RPH.  LDS: the tables take 67.5 KB per input
+// row, so M = 2 fits too; rows per half-wave go up to four (M = 1) and one
+// (M = 2, register budget of the two accumulators per row).
+template <int MR, typename XT, typename ST, typename YT, bool PRE>
+hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
+  constexpr int64_t max_rows = (MR == 1 ? 4 : 1) * LUT_HALFWAVES;
+  int64_t blocks = dev.num_cus;
+  int64_t rpb = (a.N + blocks - 1) / blocks;
+  if (rpb < 16) rpb = a.N < 16 ? a.N : 16;
+  if (rpb > max_rows) rpb = max_rows;
+  blocks = (a.N + rpb - 1) / rpb;
+  if constexpr (MR == 2) {
+    return launch_rph<MR, 1, XT, ST, YT, PRE>(a, blocks, (int)rpb);
+  } else {
+    if (rpb <= 2 * LUT_HALFWAVES) return launch_rph<MR, 2, XT, ST, YT, PRE>(a, blocks, (int)rpb);
+    return launch_rph<MR, 4, XT, ST, YT, PRE>(a, blocks, (int)rpb);
+  }
 }
 
 template <int MR, typename XT, typename ST, typename YT>

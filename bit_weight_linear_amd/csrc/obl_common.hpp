@@ -46,6 +46,21 @@ template <> struct Store<bf16_t> {
   }
 };
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_wave_base + 16*l, where lds_wave_base must be
+// the same for the whole wave.  Counted by vmcnt like any vector load.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Workgroup barrier that makes this wave's LDS writes visible but does not
+// wait for its global loads in flight (__syncthreads() also drains vmcnt).
+// s_waitcnt immediate: lgkmcnt = 0, vmcnt = 63 and expcnt = 7 (no wait).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
 // One 16x16x32 bf16 MFMA step with fp32 accumulation.
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
