@@ -24,6 +24,9 @@
 // exactly two per CU on 256 CUs.  Workgroups are dispatched round-robin over
 // the 8 XCDs, so the tile order puts all tiles of one block-row on one XCD:
 // that XCD's L2 then holds the shared activation rows.
+#include <cstdlib>
+#include <type_traits>
+
 #include "obl_common.hpp"
 #include "obl_internal.hpp"
 
@@ -273,6 +276,265 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(
   }
 }
 
+// ===========================================================================
+// Main prefill kernel (bf16 activations, 16-byte aligned): 4 waves, one per
+// SIMD, each owning a 128 (rows) x 112 (columns) output tile.
+//
+// The VALU cost of expanding signs is fixed per 16 x 32 sign fragment, and a
+// fragment feeds one MFMA per 16 rows of the wave tile, so the VALU/MFMA ratio
+// falls as the wave's row extent grows: 128 rows give 8 MFMAs per expansion.
+// The 224 fp32 accumulators per lane live in AGPRs (one wave per SIMD leaves
+// the whole 512-entry register file to it).
+//  * Activations go global -> LDS by DMA (global_load_lds_dwordx4, no VGPRs),
+//    in natural k order into an XOR-swizzled tile (16-byte chunk c of row r at
+//    slot c ^ (r & 7)), so each operand fragment is one conflict-free
+//    ds_read_b128.  Two stage buffers are distinct LDS objects and the K loop
+//    is unrolled by two, so each access names its buffer statically and the
+//    waits on the DMA are explicit s_waitcnt vmcnt(n).
+//  * Sign words are unzipped once at staging (bit 2i -> i, 2i+1 -> 16+i): the
+//    adjacent-k pairs of the natural order are then 16 bits apart, exactly
+//    what the one-shift expansion produces.  b, when present, is folded into
+//    the sign operand as bf16(b) (magnitudes, natural order).
+//  * Operands are swapped (signs = MFMA A, activations = MFMA B), so a lane's
+//    four accumulator values are four consecutive output columns of one row.
+//  * Rows past M and columns past N read clamped (valid) addresses and are not
+//    stored; k past K (last stage only) is zeroed in LDS after the DMA lands.
+// ===========================================================================
+constexpr int G2_BM = 256;
+constexpr int G2_BN = 224;
+constexpr int G2_KT = 128;
+constexpr int G2_STEPS = G2_KT / 32;                       // 4
+constexpr int G2_THREADS = 256;
+constexpr int G2_FM = 8;                                   // 16-row fragments per wave
+constexpr int G2_FN = 7;                                   // 16-column fragments per wave
+constexpr int G2_CPR = G2_KT / 8;                          // 16-byte chunks per row per stage (16)
+constexpr int G2_DMA = G2_BM * G2_CPR / G2_THREADS;        // DMA instructions per thread per stage (16)
+
+template <typename ST, typename YT, bool PRE>
+struct Gemm2 {
+  const bf16_t* __restrict__ X;
+  int64_t M, K;
+  const uint32_t* __restrict__ W;
+  int64_t N;
+  const ST* __restrict__ pre;
+  int64_t m0, n0, kw, nk;
+  int tid, wave, lane;
+  bool full_m;
+  uint32_t loff[2];     // per-lane element offset of its DMA chunk, for even / odd instructions
+  u32x4 wr;             // raw sign words of the next stage (column tid, 4 steps)
+  u32x4 br;             // raw b of the next stage (mag threads)
+
+  // Activation DMA of stage s into buffer `dst` (a [256][16] u32x4 LDS tile).
+  // Instruction i of wave w fills rows 4(16w + i) .. +3; lane l takes row
+  // + l/16 and LDS slot l % 16, i.e. global chunk (l % 16) ^ (row & 7).
+  __device__ __forceinline__ void dma(u32x4 (*dst)[G2_CPR], int64_t s) const {
+    const int64_t k0 = min(s, nk - 1) * G2_KT;
+    if (full_m) {
+#pragma unroll
+      for (int i = 0; i < G2_DMA; ++i) {
+        const int rbase = 4 * (16 * wave + i);
+        load_lds16(X + (m0 + rbase) * K + k0 + loff[i & 1], &dst[rbase][0]);
+      }
+    } else {
+      // Last row tile: rows past M re-read row M - 1 (never stored).
+#pragma unroll
+      for (int i = 0; i < G2_DMA; ++i) {
+        const int rbase = 4 * (16 * wave + i);
+        const int rr = lane >> 4;
+        const int64_t row = min(m0 + rbase + rr, M - 1);
+        load_lds16(X + row * K + k0 + (loff[i & 1] - (uint32_t)(rr * K)), &dst[rbase][0]);
+      }
+    }
+  }
+
+  // Exactly two vector loads (one without b), whatever the stage: the DMA
+  // waits below count on it.
+  __device__ __forceinline__ void load_side(int64_t s) {
+    const int64_t st = min(s, nk - 1) * G2_STEPS;
+    const int64_t n = min(n0 + min(tid, G2_BN - 1), N - 1);
+    wr = *reinterpret_cast<const u32x4*>(W + n * kw + st);
+    if constexpr (PRE) {
+      const int r = min(max(tid - G2_BN, 0), 15);
+      br = *reinterpret_cast<const u32x4*>(pre + st * 32 + 32 * (r >> 2) + 8 * (r & 3));
+    }
+  }
+
+  __device__ __forceinline__ void store_side(uint32_t (*w)[G2_BN], u32x4 (*mag)[4]) const {
+    if (tid < G2_BN) {
+      w[0][tid] = unzip_bits(wr.x);
+      w[1][tid] = unzip_bits(wr.y);
+      w[2][tid] = unzip_bits(wr.z);
+      w[3][tid] = unzip_bits(wr.w);
+    } else {
+      asm volatile("" ::"v"(wr));
+    }
+    if constexpr (PRE) {
+      const int r = tid - G2_BN;
+      if (r >= 0 && r < 16) {
+        const uint32_t h[4] = {br.x, br.y, br.z, br.w};   // 8 fp16 values
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d[j] = pack_bf16_pair(to_f32(f16_t{uint16_t(h[j] & 0xFFFFu)}), to_f32(f16_t{uint16_t(h[j] >> 16)}));
+        mag[r >> 2][r & 3] = u32x4{d[0], d[1], d[2], d[3]};
+      } else {
+        asm volatile("" ::"v"(br));
+      }
+    }
+  }
+
+};
+
+// vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding, n < 64).
+#define OBL_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+template <typename ST, typename YT, bool PRE>
+__global__ __launch_bounds__(G2_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W,
+                      int64_t N, const ST* __restrict__ pre, const ST* __restrict__ post,
+                      YT* __restrict__ Y, int mt, int nt, int xcd_groups) {
+  __shared__ u32x4 xa[G2_BM][G2_CPR];
+  __shared__ u32x4 xb[G2_BM][G2_CPR];
+  __shared__ uint32_t wsa[G2_STEPS][G2_BN];
+  __shared__ uint32_t wsb[G2_STEPS][G2_BN];
+  __shared__ u32x4 maga[G2_STEPS][4];
+  __shared__ u32x4 magb[G2_STEPS][4];
+  __shared__ float post_s[G2_BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+
+  int lin = blockIdx.x;
+  if (xcd_groups > 1) {
+    const int per = (mt * nt) / xcd_groups;
+    lin = (blockIdx.x % xcd_groups) * per + blockIdx.x / xcd_groups;
+  }
+  const int tm = lin / nt, tn = lin - (lin / nt) * nt;
+
+  Gemm2<ST, YT, PRE> G;
+  G.X = X; G.M = M; G.K = K; G.W = W; G.N = N; G.pre = pre;
+  G.m0 = (int64_t)tm * G2_BM;
+  G.n0 = (int64_t)tn * G2_BN;
+  G.kw = K >> 5;
+  G.nk = G.kw / G2_STEPS;               // K % 128 == 0 on this path
+  G.tid = tid; G.wave = wave; G.lane = lane;
+  G.full_m = G.m0 + G2_BM <= M;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int rr = lane >> 4;
+    G.loff[p] = (uint32_t)(rr * K + 8 * ((lane & 15) ^ ((4 * p + rr) & 7)));
+  }
+
+  // Prologue: side data of stage 0, output scales, DMA of stage 0.
+  G.load_side(0);
+  if (tid < G2_BN) post_s[tid] = to_f32(post[min(G.n0 + tid, N - 1)]);
+  G.store_side(wsa, maga);
+  G.dma(xa, 0);
+
+  f32x4 acc[G2_FN][G2_FM];
+#pragma unroll
+  for (int j = 0; j < G2_FN; ++j)
+#pragma unroll
+    for (int i = 0; i < G2_FM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const int xrow0 = wm * (G2_FM * 16) + l16;
+  const int wcol0 = wn * (G2_FN * 16) + l16;
+  constexpr int kIssued = G2_DMA + 1 + (PRE ? 1 : 0);   // vector memory ops issued per prefetch (exact)
+
+  auto compute = [&](u32x4 (*xs)[G2_CPR], uint32_t (*ws)[G2_BN], u32x4 (*mg)[4]) {
+    // One k-step (56 independent MFMAs) per iteration; not unrolled across
+    // steps, which would let the scheduler hoist later steps' operand reads
+    // and exhaust the VGPRs.
+#pragma unroll 1
+    for (int t = 0; t < G2_STEPS; ++t) {
+      u32x4 xf[G2_FM];
+#pragma unroll
+      for (int i = 0; i < G2_FM; ++i) xf[i] = xs[xrow0 + 16 * i][(4 * t + g) ^ (l16 & 7)];
+      const u32x4 mag = PRE ? mg[t][g] : ones;
+#pragma unroll
+      for (int j = 0; j < G2_FN; ++j) {
+        const u32x4 sf = expand_signs_scaled(ws[t][wcol0 + 16 * j] >> (4 * g), mag);
+#pragma unroll
+        for (int i = 0; i < G2_FM; ++i) acc[j][i] = mfma16x16x32(sf, xf[i], acc[j][i]);
+      }
+    }
+  };
+
+  // Stages in pairs: A (even) then B (odd).  Each half first issues the next
+  // stage's loads (two side loads, then 16 DMAs), then waits until only those
+  // are outstanding, i.e. until its own stage's DMA has landed.  The second
+  // half always prefetches stage kt+2 (clamped): for an odd stage count that
+  // is the final stage, computed after the loop; otherwise it is unused.
+  int64_t kt = 0;
+  for (; kt + 1 < G.nk; kt += 2) {
+    G.load_side(kt + 1);
+    G.dma(xb, kt + 1);
+    OBL_WAIT_VMCNT(kIssued);
+    lds_barrier();                      // stage kt visible to all
+    compute(xa, wsa, maga);
+    G.store_side(wsb, magb);
+    lds_barrier();                      // everyone is done with A and side A
+    G.load_side(kt + 2);
+    G.dma(xa, kt + 2);
+    OBL_WAIT_VMCNT(kIssued);
+    lds_barrier();
+    compute(xb, wsb, magb);
+    G.store_side(wsa, maga);
+    lds_barrier();
+  }
+  if (kt < G.nk) {                      // odd number of stages: the last one is in A
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    compute(xa, wsa, maga);
+  }
+  __builtin_amdgcn_s_waitcnt(0);        // no DMA may still target LDS when the block ends
+
+  // Epilogue: acc[j][i][r] = Y[row m0 + xrow0 + 16 i][col n0 + 112 wn + 16 j + 4 g + r].
+#pragma unroll
+  for (int i = 0; i < G2_FM; ++i) {
+    const int64_t m = G.m0 + xrow0 + 16 * i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < G2_FN; ++j) {
+      const int cl = wn * (G2_FN * 16) + j * 16 + 4 * g;   // column within the tile
+      const int64_t n = G.n0 + cl;
+      YT* yp = Y + m * N + n;
+      const float v0 = acc[j][i][0] * post_s[cl + 0], v1 = acc[j][i][1] * post_s[cl + 1];
+      const float v2 = acc[j][i][2] * post_s[cl + 2], v3 = acc[j][i][3] * post_s[cl + 3];
+      if (n + 3 < N && (reinterpret_cast<uintptr_t>(yp) & (4 * sizeof(YT) - 1)) == 0) {
+        if constexpr (sizeof(YT) == 2) {
+          *reinterpret_cast<u32x2*>(yp) = u32x2{pack_bf16_pair(v0, v1), pack_bf16_pair(v2, v3)};
+        } else {
+          *reinterpret_cast<f32x4*>(yp) = f32x4{v0, v1, v2, v3};
+        }
+      } else {
+        if (n + 0 < N) Store<YT>::put(yp + 0, v0);
+        if (n + 1 < N) Store<YT>::put(yp + 1, v1);
+        if (n + 2 < N) Store<YT>::put(yp + 2, v2);
+        if (n + 3 < N) Store<YT>::put(yp + 3, v3);
+      }
+    }
+  }
+}
+
+template <typename ST, typename YT, bool PRE>
+hipError_t launch_bf16(const LinearArgs& a) {
+  const int64_t mt = (a.M + G2_BM - 1) / G2_BM;
+  const int64_t nt = (a.N + G2_BN - 1) / G2_BN;
+  const int64_t tiles = mt * nt;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const int xcd = (tiles % 8 == 0) ? 8 : 1;
+  hipLaunchKernelGGL((gemm_bf16_kernel<ST, YT, PRE>), dim3((unsigned)tiles), dim3(G2_THREADS), 0, a.stream,
+                     static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N, static_cast<const ST*>(a.pre),
+                     static_cast<const ST*>(a.post), static_cast<YT*>(a.Y), (int)mt, (int)nt, xcd);
+  return hipGetLastError();
+}
+
 template <int AMODE, typename XT, typename ST, typename YT, bool PRE>
 hipError_t launch_t(const LinearArgs& a, const DeviceInfo&) {
   const int64_t mt = (a.M + GM_BM - 1) / GM_BM;
@@ -287,11 +549,28 @@ hipError_t launch_t(const LinearArgs& a, const DeviceInfo&) {
   return hipGetLastError();
 }
 
+// OBL_GEMM=v1 forces the original 8-wave kernel (tests compare both).
+bool gemm_force_v1() {
+  const char* e = std::getenv("OBL_GEMM");
+  return e && e[0] == 'v' && e[1] == '1';
+}
+
 template <typename ST, typename YT>
 hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
   // bf16 activations (8-byte aligned rows): A = x exactly, and the input-side
   // scale, if any, is folded into B as bf16(b).  Otherwise A is converted once
   // per staged element: bf16(x·b) or bf16(x).
+  // Main kernel: bf16 x and packed words 16-byte aligned, K % 128 == 0, b
+  // absent or fp16 and 16-byte aligned.  Everything else runs the 8-wave kernel.
+  const bool v2 = a.x_dtype == DT_BF16 && (reinterpret_cast<uintptr_t>(a.X) % 16 == 0) &&
+                  (reinterpret_cast<uintptr_t>(a.W) % 16 == 0) && a.K % G2_KT == 0 &&
+                  (!a.pre || (a.scale_dtype == DT_F16 && reinterpret_cast<uintptr_t>(a.pre) % 16 == 0));
+  if (v2 && !gemm_force_v1()) {
+    if constexpr (std::is_same<ST, f16_t>::value) {
+      if (a.pre) return launch_bf16<ST, YT, true>(a);
+    }
+    if (!a.pre) return launch_bf16<ST, YT, false>(a);
+  }
   const bool raw = a.x_dtype == DT_BF16 && (reinterpret_cast<uintptr_t>(a.X) % 8 == 0);
   if (raw) return a.pre ? launch_t<A_RAW, bf16_t, ST, YT, true>(a, dev)
                         : launch_t<A_RAW, bf16_t, ST, YT, false>(a, dev);

@@ -100,6 +100,18 @@ __device__ __forceinline__ u32x4 expand_signs_scaled(uint32_t w_shifted, u32x4 m
   return r;
 }
 
+// Perfect outer unshuffle of a 32-bit sign word: bit 2i -> bit i and bit 2i+1
+// -> bit 16+i (i < 16).  After it, the signs of the adjacent pair (k = 2i,
+// 2i+1) sit 16 bits apart, which is the pair the expansion above serves, so
+// operands stored in natural k order pair with the expanded signs.
+__device__ __forceinline__ uint32_t unzip_bits(uint32_t x) {
+  uint32_t t;
+  t = (x ^ (x >> 1)) & 0x22222222u; x = x ^ t ^ (t << 1);
+  t = (x ^ (x >> 2)) & 0x0C0C0C0Cu; x = x ^ t ^ (t << 2);
+  t = (x ^ (x >> 4)) & 0x00F000F0u; x = x ^ t ^ (t << 4);
+  return __builtin_amdgcn_perm(x, x, 0x07050604u) ;  // swap bytes 1 and 2
+}
+
 // Pack two fp32 values (already representable in bf16) into one dword.
 __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
   return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);

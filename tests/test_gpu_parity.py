@@ -87,7 +87,7 @@ def test_decode_path(M, K, N, dts):
 
 GEMM_CASES = [
     (17, 32, 16), (64, 96, 225), (255, 512, 448), (256, 4096, 224), (257, 160, 1000),
-    (600, 4096, 449), (33, 64, 33),
+    (600, 4096, 449), (33, 64, 33), (513, 384, 230), (300, 1152, 672),
 ]
 GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("f32", "f32", "f32"),
                ("f32", "f16", "bf16")]
@@ -95,8 +95,13 @@ GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("f32", "f32", "
 
 @pytest.mark.parametrize("M,K,N", GEMM_CASES)
 @pytest.mark.parametrize("dts", GEMM_DTYPES, ids=lambda d: "-".join(d))
-def test_gemm_path(M, K, N, dts):
-    G.say(f"gemm M={M} K={K} N={N} {dts}")
+@pytest.mark.parametrize("impl", ["auto", "v1"])
+def test_gemm_path(M, K, N, dts, impl, monkeypatch):
+    """impl=auto picks the 4-wave kernel where it applies (bf16 x, K % 128 == 0),
+    v1 forces the 8-wave kernel everywhere."""
+    if impl == "v1":
+        monkeypatch.setenv("OBL_GEMM", "v1")
+    G.say(f"gemm[{impl}] M={M} K={K} N={N} {dts}")
     c = WL.onebit_case(M, K, N, *dts, seed=M + 2 * K + N)
     G.check_onebit(c, G.run_onebit(c, "gemm"), "gemm")
 
@@ -186,7 +191,8 @@ def test_workload5_dbf():
 # ------------------------------------------------------------------ exact regimes
 @pytest.mark.parametrize("path,M,K,N", [("lut", 1, 4096, 1000), ("lut", 2, 8224, 77),
                                         ("decode", 16, 4096, 4096), ("decode", 9, 544, 65),
-                                        ("gemm", 300, 4096, 500), ("gemm", 2048, 1024, 448)])
+                                        ("gemm", 300, 4096, 500), ("gemm", 2048, 1024, 448),
+                                        ("gemm", 512, 640, 448), ("gemm", 96, 160, 100)])
 def test_integer_exact_bitwise(path, M, K, N):
     G.say(f"int-exact {path} M={M} K={K} N={N}")
     c = WL.onebit_case(M, K, N, "bf16", "f16", "f32", kind="int_exact", seed=K + N)
