@@ -549,10 +549,11 @@ hipError_t launch_t(const LinearArgs& a, const DeviceInfo&) {
   return hipGetLastError();
 }
 
-// OBL_GEMM=v1 forces the original 8-wave kernel (tests compare both).
-bool gemm_force_v1() {
+// OBL_GEMM=v1 / v2 force the 8-wave / the LDS-staged kernel (tests compare
+// them with the default choice).
+int gemm_forced() {
   const char* e = std::getenv("OBL_GEMM");
-  return e && e[0] == 'v' && e[1] == '1';
+  return (e && e[0] == 'v' && (e[1] == '1' || e[1] == '2')) ? e[1] - '0' : 0;
 }
 
 template <typename ST, typename YT>
@@ -565,7 +566,9 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
   const bool v2 = a.x_dtype == DT_BF16 && (reinterpret_cast<uintptr_t>(a.X) % 16 == 0) &&
                   (reinterpret_cast<uintptr_t>(a.W) % 16 == 0) && a.K % G2_KT == 0 &&
                   (!a.pre || (a.scale_dtype == DT_F16 && reinterpret_cast<uintptr_t>(a.pre) % 16 == 0));
-  if (v2 && !gemm_force_v1()) {
+  const int forced = gemm_forced();
+  if (forced == 0 && gemm_wide_eligible(a)) return launch_gemm_wide(a, dev);
+  if (v2 && forced != 1) {
     if constexpr (std::is_same<ST, f16_t>::value) {
       if (a.pre) return launch_bf16<ST, YT, true>(a);
     }

@@ -1,0 +1,346 @@
+// Main prefill kernel for M > 16 with bf16 activations:
+// Y = ((X ⊙ b) W_sign^T) ⊙ a on v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+//
+// OneBit page ("1bit量化"), proposition 1: for M > 16 the sign-binarised layer
+// is a dense contraction (2·M·N·K flops), so it belongs on the matrix cores.
+//
+// Why 32x32x16 and one wave per SIMD.  On gfx950 a single wave issuing
+// independent 16x16x32 MFMAs keeps the matrix pipe only ~60% busy, while
+// 32x32x16 MFMAs (32 cycles each) reach ~90% from one wave and tolerate about
+// four VALU ops per MFMA at ~80%.  One wave per SIMD leaves the whole
+// 512-entry register file to it: 224 fp32 accumulators in AGPRs plus the
+// operand stages in VGPRs.
+//
+// Tiling: 4 waves as 2 (rows) x 2 (columns), 64 x 224 outputs per wave
+// (2 x 7 fragments of 32 x 32), so a workgroup owns 128 x 448 outputs.  For
+// M = 2048, N = 14336 that is 16 x 32 = 512 tiles: exactly two per CU on 256
+// CUs.  Tiles are ordered so each XCD (blockIdx % 8) takes a contiguous range
+// that walks all column tiles of two row tiles: its L2 then serves one
+// 128-row activation block to 32 workgroups at a time.
+//
+// Operands, per 16-k step (MFMA A = signs, B = activations):
+//  * Activations: each 128-k stage of the workgroup's 128 rows is copied
+//    global -> LDS by DMA (buffer_load_dwordx4 ... lds, 1 KiB per
+//    instruction, fully coalesced), XOR-swizzled so that the MFMA-layout
+//    reads -- lane (row r = lane % 32, half g = lane / 32) takes
+//    x[r][16s + 8g .. 16s + 8g + 7], natural k order -- are one conflict-free
+//    ds_read_b128 each.  Loading straight into registers in MFMA layout
+//    touches 32 rows per instruction and costs the texture path ~4x more.
+//  * Signs: the stage's 4 packed words (16 bytes) per column also arrive by
+//    DMA; each wave reads its 7 columns' words once per stage.  A dword of
+//    the operand holds the pair (k, k+1); its two sign bits sit side by side
+//    in one 16-bit half of a word.  One packed 16-bit shift
+//    (v_pk_lshlrev_b16, both result halves fed from the same source half)
+//    moves bit k to bit 15 and bit k+1 to bit 31, and one v_bitop3 masks them
+//    and applies them to the magnitudes: two VALU ops per two weights, with
+//    no bit shuffling of the packed words.
+//  * Magnitudes: bf16(b_k) pairs (or 1.0 without b), converted once per
+//    workgroup into an LDS table at kernel start, one ds_read_b128 per step.
+//  * Three stage buffers, one barrier per stage: stages t + 1 and t + 2 are
+//    in flight while stage t is computed (two stages of latency cover the
+//    misses of the streamed sign words, one line per column per 8 stages).
+//  * Out-of-range rows / columns re-read the last valid one and are not
+//    stored; every load is unconditional.
+//  * Epilogue: acc·a in fp32 (a staged in LDS), one cast to the output dtype.
+//    A lane holds four consecutive output columns per register quad, written
+//    as one 16-byte (fp32) or 8-byte (bf16) store.
+#include <type_traits>
+
+#include "obl_common.hpp"
+#include "obl_internal.hpp"
+
+namespace obl {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int GW_THREADS = 256;
+constexpr int GW_BM = 128;        // workgroup rows
+constexpr int GW_BN = 448;        // workgroup columns
+constexpr int GW_WM = 64;         // wave rows
+constexpr int GW_WN = 224;        // wave columns
+constexpr int GW_FM = GW_WM / 32; // 2 activation fragments
+constexpr int GW_FN = GW_WN / 32; // 7 sign fragments
+constexpr int GW_KT = 128;        // k per stage
+constexpr int GW_S = GW_KT / 16;  // MFMA k-steps per stage
+
+// Buffer resource for a raw byte range (loads past `bytes` would return zeros;
+// the kernel clamps its offsets so none does).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Sign operand of one k-step from the 16-bit half `h` of a packed word:
+// dword j covers the pair (2j + 8g, 2j + 8g + 1) of that half, whose sign
+// bits go to bits 15 and 31 by the per-lane shift pair sh[j].
+__device__ __forceinline__ u32x4 expand_half(uint32_t h, const u16x2* sh, u32x4 mag) {
+  const u16x2 d = u16x2{(unsigned short)h, (unsigned short)h};
+  u32x4 r;
+  r.x = (__builtin_bit_cast(uint32_t, d << sh[0]) & 0x80008000u) ^ mag.x;
+  r.y = (__builtin_bit_cast(uint32_t, d << sh[1]) & 0x80008000u) ^ mag.y;
+  r.z = (__builtin_bit_cast(uint32_t, d << sh[2]) & 0x80008000u) ^ mag.z;
+  r.w = (__builtin_bit_cast(uint32_t, d << sh[3]) & 0x80008000u) ^ mag.w;
+  return r;
+}
+
+// LDS DMA of 16 bytes per lane from a buffer resource: lane l's bytes land at
+// lds_wave_base + 16 l (lds_wave_base uniform over the wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)voff, (int)soff, 0, 0);
+}
+
+constexpr int GW_XDMA = GW_BM * (GW_KT / 8) / 64 / 4;    // activation DMAs per wave per stage (8)
+constexpr int GW_WCOLS = 512;                             // sign columns staged (>= GW_BN, 2 DMAs per wave)
+constexpr int GW_WDMA = GW_WCOLS / 64 / 4;                // sign DMAs per wave per stage (2)
+
+template <typename ST, typename YT, bool PRE>
+__global__ __launch_bounds__(GW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W,
+                      int64_t N, const ST* __restrict__ pre, const ST* __restrict__ post,
+                      YT* __restrict__ Y, int mt, int nt, int xcd_groups) {
+  // Three stage buffers as distinct LDS objects: the K loop is unrolled by
+  // three so every access names its buffer, and the compiler can tell a DMA
+  // into one buffer from reads of another.
+  __shared__ u32x4 xa[GW_BM][GW_KT / 8];     // activations: row, 16-byte slot (swizzled)
+  __shared__ u32x4 xb[GW_BM][GW_KT / 8];
+  __shared__ u32x4 xc[GW_BM][GW_KT / 8];
+  __shared__ u32x4 wa[GW_WCOLS];             // 4 packed words (128 k) per column
+  __shared__ u32x4 wb[GW_WCOLS];
+  __shared__ u32x4 wc[GW_WCOLS];
+  __shared__ float post_s[GW_BN];
+  extern __shared__ uint32_t btab[];         // [K / 2] bf16(b) pairs (with b only)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS DMA bases stay scalar
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int64_t kw = K >> 5;
+  const int nk = (int)(K / GW_KT);
+  const int tiles = mt * nt;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(N * kw * 4));
+
+  // The bf16(b) table, once per workgroup: all loads of a batch are issued
+  // before any is used.
+  if constexpr (PRE) {
+    const int64_t npair = K / 2;
+    for (int64_t p0 = 0; p0 < npair; p0 += 8 * GW_THREADS) {
+      float lo[8], hi[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t pc = min(p0 + u * GW_THREADS + tid, npair - 1);
+        lo[u] = to_f32(pre[2 * pc]);
+        hi[u] = to_f32(pre[2 * pc + 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t pp = p0 + u * GW_THREADS + tid;
+        if (pp < npair) btab[pp] = pack_bf16_pair(lo[u], hi[u]);
+      }
+    }
+  }
+
+  // Shift pairs: dword j of half-group g takes bits 8g + 2j (-> 15) and
+  // 8g + 2j + 1 (-> 31) of a 16-bit half.
+  u16x2 sh[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    sh[j] = u16x2{(unsigned short)(15 - 8 * g - 2 * j), (unsigned short)(14 - 8 * g - 2 * j)};
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const u32x4* bt4 = reinterpret_cast<const u32x4*>(btab);
+  const int xrow = wm * GW_WM + l32;       // + 32 i
+  const int wcol = wn * GW_WN + l32;       // + 32 c
+
+  // XCD x (= blockIdx % 8) takes tiles [x·T/8, (x+1)·T/8), column index fastest.
+  int lin = blockIdx.x;
+  if (xcd_groups > 1) {
+    const int per = tiles / xcd_groups;
+    lin = (blockIdx.x % xcd_groups) * per + blockIdx.x / xcd_groups;
+  }
+  const int tm = lin / nt, tn = lin - (lin / nt) * nt;
+  const int64_t bm0 = (int64_t)tm * GW_BM, bn0 = (int64_t)tn * GW_BN;
+
+  // DMA offsets (bytes, < 2^32: checked by the launcher), fixed across stages.
+  // Activation DMA i of wave w fills rows 4(8w + i) .. +3 of the tile; lane l
+  // takes row + l/16 and LDS slot l % 16, i.e. global 16-byte chunk
+  // (l % 16) ^ (row % 16): chunk c of row r sits at slot c ^ (r % 16), so the
+  // 16 rows read by a half-wave fall on 16 different slots.  Rows past M
+  // re-read row M - 1, columns past N column N - 1 (never stored).
+  uint32_t xo[GW_XDMA], wo[GW_WDMA];
+#pragma unroll
+  for (int i = 0; i < GW_XDMA; ++i) {
+    const int row = 4 * (GW_XDMA * wave + i) + (lane >> 4);
+    const int64_t r = min(bm0 + row, M - 1);
+    xo[i] = (uint32_t)((r * K + 8 * ((lane & 15) ^ (row & 15))) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < GW_WDMA; ++j) {
+    const int64_t n = min(bn0 + 64 * (GW_WDMA * wave + j) + lane, N - 1);
+    wo[j] = (uint32_t)(n * kw * 4);
+  }
+  auto dma = [&](u32x4 (*xs)[GW_KT / 8], u32x4* ws, int t) {
+#pragma unroll
+    for (int i = 0; i < GW_XDMA; ++i) dma16(xr, &xs[4 * (GW_XDMA * wave + i)][0], xo[i], (uint32_t)t * (GW_KT * 2));
+#pragma unroll
+    for (int j = 0; j < GW_WDMA; ++j) dma16(wr, &ws[64 * (GW_WDMA * wave + j)], wo[j], (uint32_t)t * 16);
+  };
+
+  dma(xa, wa, 0);
+  dma(xb, wb, min(1, nk - 1));
+
+  // Output scales of this tile, while stages 0 and 1 are in flight.
+  for (int c = tid; c < GW_BN; c += GW_THREADS) post_s[c] = to_f32(post[min(bn0 + c, N - 1)]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): stages 0 and 1 landed
+  __syncthreads();
+
+  f32x16 acc[GW_FN][GW_FM];
+#pragma unroll
+  for (int c = 0; c < GW_FN; ++c)
+#pragma unroll
+    for (int i = 0; i < GW_FM; ++i) acc[c][i] = f32x16{};
+
+  // One stage.  The LDS operands of k-step s + 1 (two activation fragments
+  // and the magnitudes) are read before the MFMAs of step s are issued, so
+  // their latency hides behind step s; the scheduling barrier keeps the
+  // compiler from sinking those reads back to their use.
+  auto compute = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, int t) {
+    u32x4 wv[GW_FN];
+#pragma unroll
+    for (int c = 0; c < GW_FN; ++c) wv[c] = ws[wcol + 32 * c];
+    u32x4 xf[2][GW_FM], mg[2];
+    auto read_step = [&](int s, int b) {
+      mg[b] = PRE ? bt4[(t * GW_KT + 16 * s + 8 * g) >> 3] : ones;
+#pragma unroll
+      for (int i = 0; i < GW_FM; ++i) xf[b][i] = xs[xrow + 32 * i][(2 * s + g) ^ (lane & 15)];
+    };
+    read_step(0, 0);
+#pragma unroll
+    for (int s = 0; s < GW_S; ++s) {
+      const int b = s & 1;
+      if (s + 1 < GW_S) read_step(s + 1, b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < GW_FN; ++c) {
+        const uint32_t word = wv[c][s >> 1];
+        const u32x4 a = expand_half((s & 1) ? (word >> 16) : (word & 0xFFFFu), sh, mg[b]);
+#pragma unroll
+        for (int i = 0; i < GW_FM; ++i) acc[c][i] = mfma32(a, xf[b][i], acc[c][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One barrier per stage, prefetch distance two.  Step t issues the DMA of
+  // stage t + 2 into the buffer that stage t - 1 used (every wave finished
+  // reading it before the previous barrier), computes stage t, then waits
+  // for its own DMA of stage t + 1 (all but the GW_XDMA + GW_WDMA most recent
+  // transfers) and meets the others at the barrier, which publishes stage
+  // t + 1.  Prefetch indices are clamped: a redundant reload of the last
+  // stage into an idle buffer is harmless.
+  auto step = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, u32x4 (*xp)[GW_KT / 8], u32x4* wp, int t) {
+    dma(xp, wp, min(t + 2, nk - 1));
+    compute(xs, ws, t);
+    // vmcnt(10) lgkmcnt(0), then a bare s_barrier: __syncthreads() would also
+    // drain the prefetch of stage t + 2 (its fence waits for vmcnt(0)).
+    __builtin_amdgcn_s_waitcnt(0x0070 | (GW_XDMA + GW_WDMA));
+    __builtin_amdgcn_s_barrier();
+  };
+  static_assert(GW_XDMA + GW_WDMA < 16, "vmcnt immediate");
+  int t = 0;
+  for (; t + 3 <= nk; t += 3) {
+    step(xa, wa, xc, wc, t);
+    step(xb, wb, xa, wa, t + 1);
+    step(xc, wc, xb, wb, t + 2);
+  }
+  if (t < nk) step(xa, wa, xc, wc, t);
+  if (t + 1 < nk) step(xb, wb, xa, wa, t + 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // no DMA may still target LDS when the block ends
+
+  // Epilogue.  acc[c][i][4q + e] = D[row n = 8q + 4g + e][col m = l32] of the
+  // (c, i) fragment, i.e. Y[m0 + 32i + l32][n0 + 32c + 8q + 4g + e].
+  const int64_t m0 = bm0 + wm * GW_WM;
+#pragma unroll
+  for (int i = 0; i < GW_FM; ++i) {
+    const int64_t m = m0 + 32 * i + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int c = 0; c < GW_FN; ++c) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cl = wn * GW_WN + 32 * c + 8 * q + 4 * g;      // column within the workgroup tile
+        const int64_t n = bn0 + cl;
+        const f32x4 ps = *reinterpret_cast<const f32x4*>(post_s + cl);
+        const float v0 = acc[c][i][4 * q + 0] * ps.x, v1 = acc[c][i][4 * q + 1] * ps.y;
+        const float v2 = acc[c][i][4 * q + 2] * ps.z, v3 = acc[c][i][4 * q + 3] * ps.w;
+        YT* yp = Y + m * N + n;
+        if (n + 3 < N && (reinterpret_cast<uintptr_t>(yp) & (4 * sizeof(YT) - 1)) == 0) {
+          if constexpr (sizeof(YT) == 2) {
+            *reinterpret_cast<u32x2*>(yp) = u32x2{pack_bf16_pair(v0, v1), pack_bf16_pair(v2, v3)};
+          } else {
+            *reinterpret_cast<f32x4*>(yp) = f32x4{v0, v1, v2, v3};
+          }
+        } else {
+          if (n + 0 < N) Store<YT>::put(yp + 0, v0);
+          if (n + 1 < N) Store<YT>::put(yp + 1, v1);
+          if (n + 2 < N) Store<YT>::put(yp + 2, v2);
+          if (n + 3 < N) Store<YT>::put(yp + 3, v3);
+        }
+      }
+    }
+  }
+}
+
+template <typename ST, typename YT, bool PRE>
+hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
+  const int64_t mt = (a.M + GW_BM - 1) / GW_BM;
+  const int64_t nt = (a.N + GW_BN - 1) / GW_BN;
+  const int64_t tiles = mt * nt;
+  (void)dev;
+  const int64_t grid = tiles;
+  const int xcd = (tiles % 8 == 0) ? 8 : 1;
+  const size_t lds = (PRE ? a.K / 2 : 0) * sizeof(uint32_t);
+  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE>), dim3((unsigned)grid), dim3(GW_THREADS), lds,
+                     a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
+                     static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post),
+                     static_cast<YT*>(a.Y), (int)mt, (int)nt, xcd);
+  return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
+  if (a.y_dtype == DT_F32) return a.pre ? launch<ST, float, true>(a, dev) : launch<ST, float, false>(a, dev);
+  return a.pre ? launch<ST, bf16_t, true>(a, dev) : launch<ST, bf16_t, false>(a, dev);
+}
+
+}  // namespace
+
+bool gemm_wide_eligible(const LinearArgs& a) {
+  if (a.x_dtype != DT_BF16 || a.K % GW_KT != 0) return false;
+  if (reinterpret_cast<uintptr_t>(a.X) % 16 != 0 || reinterpret_cast<uintptr_t>(a.W) % 16 != 0) return false;
+  // Buffer byte ranges and offsets must fit in 32 bits (with room for the
+  // out-of-range sentinel), and the grid in an int.
+  const int64_t lim = (int64_t)0xFFFFF000u;
+  if (a.M * a.K * 2 > lim || a.N * (a.K / 32) * 4 > lim) return false;
+  const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GW_BN - 1) / GW_BN);
+  if (tiles > 0x7fffffff) return false;
+  // LDS: the bf16(b) table (2K bytes, dynamic) next to 122 KiB of static
+  // stage buffers.
+  return !a.pre || a.K <= 16384;
+}
+
+hipError_t launch_gemm_wide(const LinearArgs& a, const DeviceInfo& dev) {
+  return a.scale_dtype == DT_F32 ? launch_y<float>(a, dev) : launch_y<f16_t>(a, dev);
+}
+
+}  // namespace obl

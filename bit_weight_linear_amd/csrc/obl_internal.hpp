@@ -40,6 +40,9 @@ hipError_t launch_pack_signs(const void* S, int s_dtype, int64_t rows, int64_t K
 hipError_t launch_gemv_lut(const LinearArgs& a, const DeviceInfo& dev);
 hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
+// Main prefill kernel (bf16 activations); launch_gemm_mfma dispatches to it.
+bool gemm_wide_eligible(const LinearArgs& a);
+hipError_t launch_gemm_wide(const LinearArgs& a, const DeviceInfo& dev);
 
 // Largest M served by the LUT GEMV and by the decode kernel.
 constexpr int64_t kLutMaxM = 2;

@@ -89,18 +89,18 @@ GEMM_CASES = [
     (17, 32, 16), (64, 96, 225), (255, 512, 448), (256, 4096, 224), (257, 160, 1000),
     (600, 4096, 449), (33, 64, 33), (513, 384, 230), (300, 1152, 672),
 ]
-GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("f32", "f32", "f32"),
-               ("f32", "f16", "bf16")]
+GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("bf16", "f32", "bf16"),
+               ("f32", "f32", "f32"), ("f32", "f16", "bf16")]
 
 
 @pytest.mark.parametrize("M,K,N", GEMM_CASES)
 @pytest.mark.parametrize("dts", GEMM_DTYPES, ids=lambda d: "-".join(d))
-@pytest.mark.parametrize("impl", ["auto", "v1"])
+@pytest.mark.parametrize("impl", ["auto", "v2", "v1"])
 def test_gemm_path(M, K, N, dts, impl, monkeypatch):
-    """impl=auto picks the 4-wave kernel where it applies (bf16 x, K % 128 == 0),
-    v1 forces the 8-wave kernel everywhere."""
-    if impl == "v1":
-        monkeypatch.setenv("OBL_GEMM", "v1")
+    """impl=auto picks the register-staged 32x32 kernel where it applies (bf16 x,
+    K % 128 == 0), v2 the LDS-staged kernel, v1 the 8-wave kernel everywhere."""
+    if impl != "auto":
+        monkeypatch.setenv("OBL_GEMM", impl)
     G.say(f"gemm[{impl}] M={M} K={K} N={N} {dts}")
     c = WL.onebit_case(M, K, N, *dts, seed=M + 2 * K + N)
     G.check_onebit(c, G.run_onebit(c, "gemm"), "gemm")
