@@ -51,6 +51,25 @@ __device__ __forceinline__ float halfwave_sum(float v) {
   return v;
 }
 
+// Four consecutive elements (8 or 16 bytes, aligned) as fp32.
+__device__ __forceinline__ void load4(const bf16_t* p, float (&o)[4]) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const f16_t* p, float (&o)[4]) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  o[0] = to_f32(f16_t{uint16_t(v.x)}); o[1] = to_f32(f16_t{uint16_t(v.x >> 16)});
+  o[2] = to_f32(f16_t{uint16_t(v.y)}); o[3] = to_f32(f16_t{uint16_t(v.y >> 16)});
+}
+__device__ __forceinline__ void load4(const float* p, float (&o)[4]) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+
+// VEC4: K % 128 == 0 and W, X, b aligned for 16-byte sign loads and 4-element
+// X / b loads (one load per thread and input instead of four: fewer requests
+// queued ahead of the sign stream).
 template <int MR, int RPH, bool MULTI, typename XT, typename ST, typename YT, bool PRE, bool VEC4>
 __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
     const XT* __restrict__ X, int64_t K, const uint32_t* __restrict__ W, int64_t N,
@@ -81,46 +100,59 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
   // header would drain vmcnt and wait for the output-scale loads above.
   const int64_t nslab = MULTI ? K : 1;
   for (int64_t s0 = 0; s0 < nslab; s0 += LUT_SLAB_K) {
-    // Table inputs first, from every wave, then a barrier (no memory wait),
-    // then the sign words: the CU's memory pipeline serves requests in issue
-    // order, so the small, L2-resident table inputs are not queued behind the
-    // HBM-bound sign stream.  Loads are unconditional (clamped addresses).
     const int g = tid;                       // this thread's table group
     const int64_t k = s0 + 4 * g;
     const bool kval = k < K;                 // K % 32 == 0: a group is all in or all out
     const int64_t kk = kval ? k : 0;
-    float xr[MR][4], pr[4];
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr[m][i] = to_f32(X[m * K + kk + i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (PRE) pr[i] = to_f32(pre[kk + i]);
-      else pr[i] = 1.f;
-    }
-    // Barrier without a memory wait: every wave has issued its table inputs
-    // before any wave issues sign loads, and (for later slabs) every wave has
-    // finished reading the previous table.
-    __builtin_amdgcn_s_barrier();
 
     // Sign words of this lane's chunk for each of its rows.  Rows past the
     // block's last row read a clamped row and are never looked up; words past
     // K read a clamped address and meet zero table entries, so they add nothing.
     const int64_t w0 = (s0 >> 5) + 4 * c;
     u32x4 wv[RPH];
+    auto load_signs = [&]() {
 #pragma unroll
-    for (int r = 0; r < RPH; ++r) {
-      const int row = hw + LUT_HALFWAVES * r;
-      const uint32_t* src = W + (row0 + (row < nrows ? row : nrows - 1)) * kw;
-      if constexpr (VEC4) {
-        wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (w0 < kw ? w0 : kw - 4)));
-      } else {
-        uint32_t t[4];
+      for (int r = 0; r < RPH; ++r) {
+        const int row = hw + LUT_HALFWAVES * r;
+        const uint32_t* src = W + (row0 + (row < nrows ? row : nrows - 1)) * kw;
+        if constexpr (VEC4) {
+          wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (w0 < kw ? w0 : kw - 4)));
+        } else {
+          uint32_t t[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = src[w0 + i < kw ? w0 + i : kw - 1];
-        wv[r] = u32x4{t[0], t[1], t[2], t[3]};
+          for (int i = 0; i < 4; ++i) t[i] = src[w0 + i < kw ? w0 + i : kw - 1];
+          wv[r] = u32x4{t[0], t[1], t[2], t[3]};
+        }
       }
+    };
+
+    float xr[MR][4], pr[4];
+    {
+      // Table inputs first, from every wave, then a barrier (no memory wait),
+      // then the sign words: the CU's memory pipeline serves requests in issue
+      // order, so the small, L2-resident table inputs are not queued behind the
+      // HBM-bound sign stream.  Loads are unconditional (clamped addresses).
+      if constexpr (VEC4) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) load4(X + m * K + kk, xr[m]);
+        if constexpr (PRE) load4(pre + kk, pr);
+        else pr[0] = pr[1] = pr[2] = pr[3] = 1.f;
+      } else {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xr[m][i] = to_f32(X[m * K + kk + i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (PRE) pr[i] = to_f32(pre[kk + i]);
+          else pr[i] = 1.f;
+        }
+      }
+      // Barrier without a memory wait: every wave has issued its table inputs
+      // before any wave issues sign loads, and (for later slabs) every wave has
+      // finished reading the previous table.
+      __builtin_amdgcn_s_barrier();
+      load_signs();
     }
 
     // Table for this slab.  Thread tid owns group g (k = s0 + 4g .. +3).
@@ -184,7 +216,9 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
 
 template <int MR, int RPH, typename XT, typename ST, typename YT, bool PRE>
 hipError_t launch_rph(const LinearArgs& a, int64_t blocks, int rpb) {
-  const bool vec4 = (a.K % 128 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0);
+  const bool vec4 = (a.K % 128 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(a.X) % (4 * sizeof(XT)) == 0) &&
+                    (!a.pre || reinterpret_cast<uintptr_t>(a.pre) % (4 * sizeof(ST)) == 0);
   auto X = static_cast<const XT*>(a.X);
   auto pre = static_cast<const ST*>(a.pre);
   auto post = static_cast<const ST*>(a.post);

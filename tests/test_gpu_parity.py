@@ -57,7 +57,7 @@ def test_pack_largest_config_shape():
 # ------------------------------------------------------------------ parity sweeps per path
 LUT_CASES = [
     (1, 32, 1), (1, 96, 33), (2, 128, 257), (1, 4128, 300), (2, 8192, 200), (1, 4096, 4099),
-    (2, 544, 130), (1, 4096, 17),
+    (2, 544, 130), (1, 4096, 17), (1, 128, 64), (1, 2048, 513), (1, 3968, 100),
 ]
 DTYPE_COMBOS = [("bf16", "f16", "f32"), ("f32", "f32", "f32"), ("bf16", "f16", "bf16"),
                 ("f32", "f16", "f32")]
