@@ -186,10 +186,13 @@ def main():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the benchmark, run one plain device-to-device copy of this many MiB "
+                         "(a reference kernel of known traffic for hardware-counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layer would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the layer has no multi-GPU path here (one GPU holds a "
+              "whole layer's packed weights); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -279,10 +282,20 @@ def main():
         wb5 = c5.Kmid * (c5.K + c5.N) / 8
         sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
                         "parity_max_normalised_error": float(f"{e5:.3e}"), "copies": R5,
-                        "launches_per_call": 2}
+                        "stages_per_call": 2}
         log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
         del l5, t5
         out["secondary"] = sec
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = nbytes
+        del src, dst
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(WL, O)
