@@ -16,196 +16,313 @@
 //   mode B1 (bf16 x, no b):   A = x, B = ±1, 1 MFMA per step;
 //   mode S3 (fp32 x or fp32 b): x' = x·b in fp32, split exactly into three
 //       bf16 terms hi + mid + lo (24 significant bits), B = ±1, 3 MFMAs.
-// The sign operand is expanded in registers from the packed words (pair
-// order, obl_common.hpp).
+// The sign operand is expanded in registers from the packed words.
 //
 // Work split: block = 4 waves x 16 columns (64 output columns) x one K-slice
-// of 512 k, so each block reads only its slice of X.  With one slice the
+// of 512 k, so each block reads only its slice of X (a whole-K block would pull
+// all of X through every CU's L1, which measured slower).  With one slice the
 // block applies the post scale and writes Y; otherwise slices write fp32
 // partial sums to scratch and a second small kernel adds them in slice order
 // (the kernel boundary orders the memory traffic; no fences, no atomics), so
-// results are bitwise reproducible.
+// results are bitwise reproducible.  (Counting the slices in and letting the
+// last one reduce needs system-coherent stores, atomics and loads across the
+// XCDs, three memory round trips, and measured slower than the second launch.)
+//
+// Staging (all in LDS, one barrier):
+//  * the X slice (bf16 modes: by DMA, global_load_lds_dwordx4, 1 KiB per
+//    instruction, coalesced rows), natural k order, 16-byte chunk c of row r at slot
+//    c ^ (r % 16): an A fragment -- lane (row m = lane % 16, quarter g =
+//    lane / 16) takes x[m][32t + 8g .. +7] -- is one conflict-free
+//    ds_read_b128;
+//  * the 64 columns' sign words with one 16-byte load per thread, transposed
+//    into [step][column] (stride 65 words) so a wave's 16 columns of one step
+//    are 16 consecutive banks;
+//  * mode B2: the slice's (b_hi, b_lo) bf16 pair tables; mode S3: the three
+//    bf16 terms of x·b, split once per block (the four waves share them).
+// Sign expansion in natural k order: dword r of quarter g pairs k = 32t + 8g +
+// 2r and k + 1, whose sign bits sit side by side in half g / 2 of word t; one
+// packed 16-bit shift (v_pk_lshlrev_b16, both halves fed from that half) puts
+// them at bits 15 and 31 and one v_bitop3 applies them to the magnitudes.
+// The contraction takes four steps at a time: all LDS reads of the four are
+// issued before the first MFMA and each step owns its accumulators.
+#include <cstdlib>
+
 #include "obl_common.hpp"
 #include "obl_internal.hpp"
 
 namespace obl {
 namespace {
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_BN = 64;      // output columns per block (16 per wave)
 constexpr int DEC_STEPS = 16;   // 32-k steps per K-slice
-constexpr int DEC_SLOTS = DEC_STEPS * 64;
-constexpr int DEC_SLOTS_PER_THREAD = DEC_SLOTS / DEC_THREADS;
+constexpr int DEC_SK = DEC_STEPS * 32;          // k per slice
+constexpr int DEC_WSTRIDE = DEC_BN + 1;         // words per step row of the sign table
 
 enum DecMode { MODE_B2 = 0, MODE_B1 = 1, MODE_S3 = 2 };
 
-template <int MODE> struct DecTerms { static constexpr int A = (MODE == MODE_S3) ? 3 : 1; };
-
-__device__ __forceinline__ u32x4 interleave_runs(u32x2 r0, u32x2 r1) {
-  u32x4 o;
-  o.x = __builtin_amdgcn_perm(r1.x, r0.x, 0x05040100u);
-  o.y = __builtin_amdgcn_perm(r1.x, r0.x, 0x07060302u);
-  o.z = __builtin_amdgcn_perm(r1.y, r0.y, 0x05040100u);
-  o.w = __builtin_amdgcn_perm(r1.y, r0.y, 0x07060302u);
-  return o;
+// B operand of one step for quarter g: dword r takes bits p = 8(g & 1) + 2r and
+// p + 1 of the 16-bit half g / 2 of the word (sh[r] = (15 - p, 14 - p)).
+__device__ __forceinline__ u32x4 expand_nat(uint32_t word, int h, const u16x2* sh, u32x4 mag) {
+  const uint32_t half = h ? (word >> 16) : (word & 0xFFFFu);
+  const u16x2 d = u16x2{(unsigned short)half, (unsigned short)half};
+  u32x4 r;
+  r.x = (__builtin_bit_cast(uint32_t, d << sh[0]) & 0x80008000u) ^ mag.x;
+  r.y = (__builtin_bit_cast(uint32_t, d << sh[1]) & 0x80008000u) ^ mag.y;
+  r.z = (__builtin_bit_cast(uint32_t, d << sh[2]) & 0x80008000u) ^ mag.z;
+  r.w = (__builtin_bit_cast(uint32_t, d << sh[3]) & 0x80008000u) ^ mag.w;
+  return r;
 }
 
-template <int MODE, typename XT, typename ST, typename YT, bool PRE, bool VEC4>
+// FAST: X and W 16-byte aligned and K % 128 == 0 (DMA / vector loads, one
+// 16-byte sign load per thread); otherwise plain element loads.
+template <int MODE, typename XT, typename ST, typename YT, bool PRE, bool FAST>
 __global__ __launch_bounds__(DEC_THREADS) void decode_mfma_kernel(
     const XT* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, int nslices,
     float* __restrict__ partials) {
-  constexpr int TA = DecTerms<MODE>::A;
-  __shared__ u32x4 afrag[TA][DEC_STEPS][64];
-  __shared__ u32x4 mag[DEC_STEPS][4][2];  // mode B2: (b_hi, b_lo) bf16 pairs per (step, lane group)
+  constexpr int TA = MODE == MODE_S3 ? 3 : 1;          // bf16 A term arrays
+  constexpr int CPR = DEC_SK * 2 / 16;                 // 16-byte chunks (8 bf16) per row of a term array
+  __shared__ u32x4 xs[TA][16 * CPR];
+  __shared__ uint32_t ws[DEC_STEPS * DEC_WSTRIDE];
+  __shared__ uint32_t ms[MODE == MODE_B2 ? DEC_SK : 1];   // B2: (b_hi) pairs then (b_lo) pairs
 
   const int tile = blockIdx.x / nslices;
   const int slice = blockIdx.x - tile * nslices;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15;
   const int g = lane >> 4;
   const int64_t kw = K >> 5;
   const int64_t step0 = (int64_t)slice * DEC_STEPS;
+  const int64_t k0 = step0 * 32;
   const int nsteps = (int)min((int64_t)DEC_STEPS, kw - step0);
+  const int64_t n0 = (int64_t)tile * DEC_BN;
+  const int xslots = M * CPR;                          // slot q = (row q / CPR, slot q % CPR)
 
-  // ---- 1. Issue every global load of the block, branch-free.
-  // A operand (slot = (step t, lane l)): rows m = l % 16, k runs 4g..4g+3 and 4g+16..4g+19.
-  u32x2 xr0[DEC_SLOTS_PER_THREAD], xr1[DEC_SLOTS_PER_THREAD];   // bf16 modes
-  float xs[DEC_SLOTS_PER_THREAD][8];                              // S3 mode
-  uint32_t aval = 0;
-#pragma unroll
-  for (int i = 0; i < DEC_SLOTS_PER_THREAD; ++i) {
-    const int slot = tid + DEC_THREADS * i;
-    const int t = slot >> 6, l = slot & 63;
-    const int m = l & 15, gg = l >> 4;
-    const bool ok = t < nsteps && m < M;
-    aval |= uint32_t(ok) << i;
-    const int64_t kb = (step0 + t) * 32 + 4 * gg;
-    const XT* xp = X + (ok ? (int64_t)m * K + kb : 0);
-    if constexpr (MODE != MODE_S3) {
-      xr0[i] = *reinterpret_cast<const u32x2*>(xp);
-      xr1[i] = *reinterpret_cast<const u32x2*>(xp + 16);
-    } else {
-      const ST* pp = pre + (ok ? kb : 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float lo = to_f32(xp[j]), hi = to_f32(xp[j + 16]);
-        if constexpr (PRE) {
-          lo *= to_f32(pp[j]);
-          hi *= to_f32(pp[j + 16]);
-        }
-        xs[i][j] = lo;
-        xs[i][4 + j] = hi;
-      }
+  // ---- 1. Raw bf16 X (modes B1, B2) by DMA: slot (r, s) receives chunk
+  // s ^ (r % 16) of the row's slice; chunks past K re-read chunk 0 (never used).
+  if constexpr (MODE != MODE_S3 && FAST) {
+    const int rounds = (xslots + DEC_THREADS - 1) / DEC_THREADS;
+    for (int i = 0; i < rounds; ++i) {
+      const int base = (i * (DEC_THREADS / 64) + wave) * 64;
+      const int q = min(base + lane, xslots - 1);
+      const int r = q / CPR, sl = q - r * CPR;
+      int64_t ke = k0 + 8 * (int64_t)(sl ^ (r & 15));
+      if (ke >= K) ke = k0;
+      load_lds16(X + (int64_t)r * K + ke, &xs[0][base]);
     }
   }
-  // Sign words of this lane's column for the slice.
-  const int64_t col = (int64_t)tile * DEC_BN + wave * 16 + (lane & 15);
-  const bool colok = col < N;
-  uint32_t wreg[DEC_STEPS];
-  {
-    const uint32_t* src = W + (colok ? col : 0) * kw + step0;
+  // Mode S3: x and b of this thread's slots, loaded now and split after the
+  // sign loads are issued.  Slots: q = tid + 256 i.
+  constexpr int S3N = MODE == MODE_S3 ? (16 * CPR) / DEC_THREADS : 1;   // 4
+  float xv[S3N][8];
+  if constexpr (MODE == MODE_S3) {
 #pragma unroll
-    for (int q = 0; q < DEC_STEPS / 4; ++q) {
-      if (VEC4) {
-        const bool ok = colok && 4 * q < nsteps;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + (4 * q < nsteps ? 4 * q : 0));
-        wreg[4 * q + 0] = ok ? v.x : 0u;
-        wreg[4 * q + 1] = ok ? v.y : 0u;
-        wreg[4 * q + 2] = ok ? v.z : 0u;
-        wreg[4 * q + 3] = ok ? v.w : 0u;
+    for (int i = 0; i < S3N; ++i) {
+      const int q = tid + DEC_THREADS * i;
+      const int r = q / CPR, sl = q - r * CPR;
+      const int64_t ke = k0 + 8 * (int64_t)(sl ^ (r & 15));
+      const bool ok = q < xslots && ke < K;
+      const int64_t kc = ok ? ke : 0;
+      const XT* xp = X + (ok ? (int64_t)r * K : 0) + kc;
+      if constexpr (FAST && sizeof(XT) == 4) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(xp), v1 = *reinterpret_cast<const f32x4*>(xp + 4);
+        xv[i][0] = v0.x; xv[i][1] = v0.y; xv[i][2] = v0.z; xv[i][3] = v0.w;
+        xv[i][4] = v1.x; xv[i][5] = v1.y; xv[i][6] = v1.z; xv[i][7] = v1.w;
+      } else if constexpr (FAST) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xp);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[i][2 * e] = __uint_as_float(d[e] << 16);
+          xv[i][2 * e + 1] = __uint_as_float(d[e] & 0xFFFF0000u);
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = colok && 4 * q + i < nsteps;
-          const uint32_t v = src[4 * q + i < nsteps ? 4 * q + i : 0];
-          wreg[4 * q + i] = ok ? v : 0u;
-        }
+        for (int e = 0; e < 8; ++e) xv[i][e] = to_f32(xp[e]);
+      }
+      if constexpr (PRE) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[i][e] *= to_f32(pre[kc + e]);
+      }
+      if (!ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[i][e] = 0.f;
       }
     }
   }
-  // Mode B2: b for (step, lane group) = tid < 64.
-  float bl[8];
-  const bool magok = tid < DEC_STEPS * 4 && (tid >> 2) < nsteps;
-  if constexpr (MODE == MODE_B2) {
-    const int64_t kb = (step0 + (tid >> 2)) * 32 + 4 * (tid & 3);
-    const ST* pp = pre + (magok ? kb : 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bl[j] = to_f32(pp[j]);
-      bl[4 + j] = to_f32(pp[j + 16]);
-    }
-  }
-  const float post_c = to_f32(post[colok ? col : 0]);
-
-  // ---- 2. Operands into LDS.
-#pragma unroll
-  for (int i = 0; i < DEC_SLOTS_PER_THREAD; ++i) {
-    const int slot = tid + DEC_THREADS * i;
-    const int t = slot >> 6, l = slot & 63;
-    const bool ok = (aval >> i) & 1u;
-    if constexpr (MODE != MODE_S3) {
-      const u32x4 v = interleave_runs(xr0[i], xr1[i]);
-      afrag[0][t][l] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+  // ---- 2. Sign words: thread -> (column tid / 4, quad tid % 4 of the slice).
+  u32x4 wq;
+  {
+    const int col = tid >> 2, quad = tid & 3;
+    const int64_t n = min(n0 + col, N - 1);
+    const uint32_t* src = W + n * kw + step0;
+    if constexpr (FAST) {
+      const int qq = 4 * quad < nsteps ? 4 * quad : 0;
+      wq = *reinterpret_cast<const u32x4*>(src + qq);
     } else {
-      uint32_t h[4], md[4], lw[4];
+      uint32_t t4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const Split3 sa = split3(ok ? xs[i][j] : 0.f), sb = split3(ok ? xs[i][4 + j] : 0.f);
-        h[j] = pack_bf16_pair(sa.hi, sb.hi);
-        md[j] = pack_bf16_pair(sa.mid, sb.mid);
-        lw[j] = pack_bf16_pair(sa.lo, sb.lo);
+      for (int e = 0; e < 4; ++e) {
+        const int st = 4 * quad + e;
+        t4[e] = src[st < nsteps ? st : 0];
       }
-      afrag[0][t][l] = u32x4{h[0], h[1], h[2], h[3]};
-      afrag[TA > 1 ? 1 : 0][t][l] = u32x4{md[0], md[1], md[2], md[3]};
-      afrag[TA > 2 ? 2 : 0][t][l] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+      wq = u32x4{t4[0], t4[1], t4[2], t4[3]};
     }
   }
+  // ---- 3. Mode B2: the slice's b, thread -> k pair (2 tid, 2 tid + 1).
+  float b0 = 0.f, b1 = 0.f;
   if constexpr (MODE == MODE_B2) {
-    if (tid < DEC_STEPS * 4) {
-      uint32_t hi[4], lo[4];
+    const int64_t k = k0 + 2 * tid;
+    const int64_t kc = k < K ? k : 0;
+    b0 = to_f32(pre[kc]);
+    b1 = to_f32(pre[kc + 1]);
+    if (k >= K) b0 = b1 = 0.f;
+  }
+  const float post_c = to_f32(post[min(n0 + 16 * wave + j, N - 1)]);
+
+  // ---- 4. Remaining LDS writes, then one barrier.
+  if constexpr (MODE != MODE_S3 && !FAST) {
+    // Element loads into the same swizzled slots (any alignment).
+    for (int q = tid; q < xslots; q += DEC_THREADS) {
+      const int r = q / CPR, sl = q - r * CPR;
+      const int64_t ke = k0 + 8 * (int64_t)(sl ^ (r & 15));
+      const uint16_t* xr = reinterpret_cast<const uint16_t*>(X) + (int64_t)r * K;
+      uint32_t d[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = magok ? bl[j] : 0.f, a1 = magok ? bl[4 + j] : 0.f;
-        const float h0 = bf16_round(a0), h1 = bf16_round(a1);
-        hi[j] = pack_bf16_pair(h0, h1);
-        lo[j] = pack_bf16_pair(a0 - h0, a1 - h1);  // exact: fp16 residual fits bf16
+      for (int e = 0; e < 4; ++e) {
+        const int64_t k = ke + 2 * e;
+        d[e] = k < K ? (uint32_t(xr[k]) | (uint32_t(xr[k + 1]) << 16)) : 0u;
       }
-      mag[tid >> 2][tid & 3][0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      mag[tid >> 2][tid & 3][1] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      xs[0][q] = u32x4{d[0], d[1], d[2], d[3]};
     }
+  }
+  if constexpr (MODE == MODE_S3) {
+    // x' = x·b split exactly into three bf16 terms (24 significant bits).
+#pragma unroll
+    for (int i = 0; i < S3N; ++i) {
+      const int q = tid + DEC_THREADS * i;
+      uint32_t th[4], tm[4], tl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const Split3 s0 = split3(xv[i][2 * e]), s1 = split3(xv[i][2 * e + 1]);
+        th[e] = pack_bf16_pair(s0.hi, s1.hi);
+        tm[e] = pack_bf16_pair(s0.mid, s1.mid);
+        tl[e] = pack_bf16_pair(s0.lo, s1.lo);
+      }
+      if (q < xslots) {
+        xs[0][q] = u32x4{th[0], th[1], th[2], th[3]};
+        xs[TA > 1 ? 1 : 0][q] = u32x4{tm[0], tm[1], tm[2], tm[3]};
+        xs[TA > 2 ? 2 : 0][q] = u32x4{tl[0], tl[1], tl[2], tl[3]};
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every load of this thread landed
+  {
+    const int col = tid >> 2, quad = tid & 3;
+    uint32_t* d = ws + (4 * quad) * DEC_WSTRIDE + col;
+    const bool ok = 4 * quad < nsteps;
+    d[0] = ok ? wq.x : 0u;
+    d[DEC_WSTRIDE] = ok ? wq.y : 0u;
+    d[2 * DEC_WSTRIDE] = ok ? wq.z : 0u;
+    d[3 * DEC_WSTRIDE] = ok ? wq.w : 0u;
+  }
+  if constexpr (MODE == MODE_B2) {
+    const float h0 = bf16_round(b0), h1 = bf16_round(b1);
+    ms[tid] = pack_bf16_pair(h0, h1);
+    ms[DEC_SK / 2 + tid] = pack_bf16_pair(b0 - h0, b1 - h1);   // exact: an fp16 residual fits bf16
   }
   __syncthreads();
 
-  // ---- 3. Contraction: two independent accumulators (even / odd steps).
-  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  // ---- 5. Contraction: this wave's 16 columns over the slice, four steps at
+  // a time (every LDS read of the four before the first MFMA; each step owns
+  // its accumulators).
+  u16x2 sh[4];
 #pragma unroll
-  for (int t = 0; t < DEC_STEPS; ++t) {
-    if (t < nsteps) {
-      const uint32_t ws = wreg[t] >> (4 * g);
-      f32x4& acc = (t & 1) ? acc1 : acc0;
+  for (int r = 0; r < 4; ++r) {
+    const int p = 8 * (g & 1) + 2 * r;
+    sh[r] = u16x2{(unsigned short)(15 - p), (unsigned short)(14 - p)};
+  }
+  const int h = g >> 1;
+  const bool mrow = j < M;
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const int xrow = (mrow ? j : 0) * CPR;
+  const int swz = j & 15;
+  const int wcol = 16 * wave + j;
+  constexpr int NA = MODE == MODE_B1 ? 1 : 2;
+
+  f32x4 acc[4][NA];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[u][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int t = 0; t < DEC_STEPS; t += 4) {
+    uint32_t word[4];
+    u32x4 xf[4][TA], mh[4], ml[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      word[u] = ws[(t + u) * DEC_WSTRIDE + wcol];
+      const int kb = 32 * (t + u) + 8 * g;             // first k of this lane's quarter
+#pragma unroll
+      for (int ta = 0; ta < TA; ++ta) xf[u][ta] = xs[ta][xrow + ((kb / 8) ^ swz)];
       if constexpr (MODE == MODE_B2) {
-        const u32x4 a = afrag[0][t][lane];
-        acc = mfma16x16x32(a, expand_signs_scaled(ws, mag[t][g][0]), acc);
-        acc = mfma16x16x32(a, expand_signs_scaled(ws, mag[t][g][1]), acc);
-      } else {
-        const u32x4 b = expand_signs_pm1(ws);
+        mh[u] = *reinterpret_cast<const u32x4*>(ms + kb / 2);
+        ml[u] = *reinterpret_cast<const u32x4*>(ms + DEC_SK / 2 + kb / 2);
+      }
+    }
 #pragma unroll
-        for (int u = 0; u < TA; ++u) acc = mfma16x16x32(afrag[u][t][lane], b, acc);
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = mrow && (t + u < nsteps);
+      if constexpr (MODE == MODE_B2) {
+        const u32x4 a = ok ? xf[u][0] : zero4;
+        acc[u][0] = mfma16x16x32(a, expand_nat(word[u], h, sh, mh[u]), acc[u][0]);
+        acc[u][1] = mfma16x16x32(a, expand_nat(word[u], h, sh, ml[u]), acc[u][1]);
+      } else if constexpr (MODE == MODE_B1) {
+        const u32x4 a = ok ? xf[u][0] : zero4;
+        acc[u][0] = mfma16x16x32(a, expand_nat(word[u], h, sh, ones), acc[u][0]);
+      } else {
+        const u32x4 bsg = expand_nat(word[u], h, sh, ones);
+        acc[u][0] = mfma16x16x32(ok ? xf[u][0] : zero4, bsg, acc[u][0]);
+        acc[u][1] = mfma16x16x32(ok ? xf[u][1] : zero4, bsg, acc[u][1]);
+        acc[u][0] = mfma16x16x32(ok ? xf[u][2] : zero4, bsg, acc[u][0]);
       }
     }
   }
-  const f32x4 acc = acc0 + acc1;
-
-  // ---- 4. Output: lane holds rows 4g .. 4g+3 of column `col`.
-  if (!colok) return;
+  // Fixed summation order: terms of a step, then steps in order.
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * g + i;
-    if (m >= M) break;
-    if (nslices == 1) Store<YT>::put(&Y[(int64_t)m * N + col], acc[i] * post_c);
-    else partials[((int64_t)slice * M + m) * N + col] = acc[i];
+  for (int u = 0; u < 4; ++u) {
+    f32x4 su = acc[u][0];
+#pragma unroll
+    for (int a = 1; a < NA; ++a) su = su + acc[u][a];
+    tot = tot + su;
+  }
+
+  // ---- 6. Output: lane holds rows 4g .. 4g+3 of column n0 + wcol.
+  const int64_t col = n0 + wcol;
+  if (nslices == 1) {
+    if (col < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < M) Store<YT>::put(&Y[(int64_t)m * N + col], tot[i] * post_c);
+      }
+    }
+    return;
+  }
+  if (col < N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M) partials[((int64_t)slice * M + m) * N + col] = tot[i];
+    }
   }
 }
 
@@ -242,14 +359,15 @@ hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
     hipError_t e = scratch_reserve(dev.device, (size_t)(nslices * a.M * a.N), &sc);
     if (e != hipSuccess) return e;
   }
-  const bool vec4 = (kw % 4 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0);
+  const bool fast = (kw % 4 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(a.X) % 16 == 0);
   const int64_t blocks = tiles * nslices;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   auto X = static_cast<const XT*>(a.X);
   auto pre = static_cast<const ST*>(a.pre);
   auto post = static_cast<const ST*>(a.post);
   auto Y = static_cast<YT*>(a.Y);
-  if (vec4)
+  if (fast)
     hipLaunchKernelGGL((decode_mfma_kernel<MODE, XT, ST, YT, PRE, true>), dim3((unsigned)blocks),
                        dim3(DEC_THREADS), 0, a.stream, X, (int)a.M, a.K, a.W, a.N, pre, post, Y,
                        (int)nslices, sc.partials);
@@ -267,8 +385,8 @@ hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
 
 template <typename ST, typename YT>
 hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
-  // bf16 x with an 8-byte aligned base: A is x itself.
-  const bool raw = a.x_dtype == DT_BF16 && (reinterpret_cast<uintptr_t>(a.X) % 8 == 0);
+  // bf16 x: A is x itself (any alignment: the staging copies it to LDS).
+  const bool raw = a.x_dtype == DT_BF16;
   if (raw && !a.pre) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
   if (raw && a.scale_dtype == DT_F16) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);
   if (a.x_dtype == DT_BF16)
