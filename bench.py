@@ -155,6 +155,28 @@ def dbf_setup(torch, B, WL, O, rotate_bytes):
     return c, launches, err, R
 
 
+def dbf_prefill_setup(torch, B, WL, O, M=512, K=4096, Kmid=3072, N=4096, copies=8):
+    """DBF prefill (two MFMA GEMMs with the m mid-scale), sampled-row parity."""
+    import numpy as np
+    c = WL.dbf_case(M, K, Kmid, N, seed=Kmid, name=f"dbf-prefill-{M}x{K}-{Kmid}-{N}")
+    dev = torch.device("cuda")
+    X = torch.from_numpy(c.X).to(torch.float32).to(torch.bfloat16).to(dev)
+    sc = [torch.from_numpy(v).to(torch.float32).to(torch.float16).to(dev) for v in (c.b, c.m, c.a)]
+    S2 = B.pack_signs(torch.from_numpy(c.S2).to(dev))
+    S1 = B.pack_signs(torch.from_numpy(c.S1).to(dev))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((M, Kmid), dtype=torch.float32, device=dev)
+    B.dbf_linear(X, S2, S1, *sc, workspace=ws, out=Y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(1).choice(M, 16, replace=False), [0, M - 1]]))
+    err = O.max_normalised_error(Y.float().cpu().numpy().astype(np.float64)[rows],
+                                 O.dbf_linear(c.X[rows], c.S1, c.S2, c.a, c.m, c.b),
+                                 O.dbf_error_scale(c.X[rows], c.b, c.m, c.a))
+    reps = [(S2, S1)] + [(S2.clone(), S1.clone()) for _ in range(copies - 1)]
+    launches = [(lambda s2=s2, s1=s1: B.dbf_linear(X, s2, s1, *sc, workspace=ws, out=Y)) for (s2, s1) in reps]
+    return c, launches, err, copies
+
+
 def cpu_baseline(WL, O, budget_s: float = 12.0):
     """Time the fp64 oracle on workload 2 (the headline) for a bounded sample."""
     import numpy as np
@@ -285,6 +307,18 @@ def main():
                         "stages_per_call": 2}
         log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
         del l5, t5
+        # DBF prefill (M = 512, Kmid = 3072: 1.5 sign bits per weight)
+        c6, l6, e6, R6 = dbf_prefill_setup(torch, B, WL, O)
+        assert e6 <= 1.2e-2, "parity failed on the DBF prefill"
+        t6 = Timed(torch, l6)
+        _, ms6 = t6.run(2, max(3, args.steps // 4))
+        fl6 = 2.0 * c6.X.shape[0] * c6.S2.shape[0] * (c6.S2.shape[1] + c6.S1.shape[0])
+        tf6 = fl6 / (ms6 * 1e-3) / 1e12
+        sec[c6.name] = {"us_per_call": round(ms6 * 1e3, 2), "TOPS": round(tf6, 2),
+                        "mfma_frac": round(tf6 / BF16_PEAK_TFLOPS, 4),
+                        "parity_max_normalised_error_sampled": float(f"{e6:.3e}"), "copies": R6}
+        log(f"[bench] {c6.name}: {ms6 * 1e3:.1f} us per call, {tf6:.1f} TFLOP/s")
+        del l6, t6
         out["secondary"] = sec
 
     if args.copy_calibration_mib > 0:

@@ -105,7 +105,7 @@ template <typename ST, typename YT, bool PRE>
 __global__ __launch_bounds__(GW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W,
                       int64_t N, const ST* __restrict__ pre, const ST* __restrict__ post,
-                      YT* __restrict__ Y, int mt, int nt, int xcd_groups) {
+                      YT* __restrict__ Y, bf16_t* __restrict__ Y2, int mt, int nt, int xcd_groups) {
   // Three stage buffers as distinct LDS objects: the K loop is unrolled by
   // three so every access names its buffer, and the compiler can tell a DMA
   // into one buffer from reads of another.
@@ -284,6 +284,18 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
         const float v0 = acc[c][i][4 * q + 0] * ps.x, v1 = acc[c][i][4 * q + 1] * ps.y;
         const float v2 = acc[c][i][4 * q + 2] * ps.z, v3 = acc[c][i][4 * q + 3] * ps.w;
         YT* yp = Y + m * N + n;
+        if (Y2) {
+          // bf16 copy of the same fp32 results (the next DBF stage's operand).
+          bf16_t* y2 = Y2 + m * N + n;
+          if (n + 3 < N && (reinterpret_cast<uintptr_t>(y2) & 7) == 0) {
+            *reinterpret_cast<u32x2*>(y2) = u32x2{pack_bf16_pair(v0, v1), pack_bf16_pair(v2, v3)};
+          } else {
+            if (n + 0 < N) Store<bf16_t>::put(y2 + 0, v0);
+            if (n + 1 < N) Store<bf16_t>::put(y2 + 1, v1);
+            if (n + 2 < N) Store<bf16_t>::put(y2 + 2, v2);
+            if (n + 3 < N) Store<bf16_t>::put(y2 + 3, v3);
+          }
+        }
         if (n + 3 < N && (reinterpret_cast<uintptr_t>(yp) & (4 * sizeof(YT) - 1)) == 0) {
           if constexpr (sizeof(YT) == 2) {
             *reinterpret_cast<u32x2*>(yp) = u32x2{pack_bf16_pair(v0, v1), pack_bf16_pair(v2, v3)};
@@ -313,7 +325,7 @@ hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
   hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE>), dim3((unsigned)grid), dim3(GW_THREADS), lds,
                      a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                      static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post),
-                     static_cast<YT*>(a.Y), (int)mt, (int)nt, xcd);
+                     static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.Y2), (int)mt, (int)nt, xcd);
   return hipGetLastError();
 }
 
@@ -326,8 +338,15 @@ hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
 }  // namespace
 
 bool gemm_wide_eligible(const LinearArgs& a) {
-  if (a.x_dtype != DT_BF16 || a.K % GW_KT != 0) return false;
-  if (reinterpret_cast<uintptr_t>(a.X) % 16 != 0 || reinterpret_cast<uintptr_t>(a.W) % 16 != 0) return false;
+  if (a.x_dtype != DT_BF16) return false;
+  return gemm_wide_shape_ok(a.M, a.K, a.N, a.pre != nullptr, a.X, a.W);
+}
+
+bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const void* X, const void* W) {
+  LinearArgs a{};
+  a.M = M; a.K = K; a.N = N; a.pre = has_pre ? X : nullptr;
+  if (a.K % GW_KT != 0) return false;
+  if (reinterpret_cast<uintptr_t>(X) % 16 != 0 || reinterpret_cast<uintptr_t>(W) % 16 != 0) return false;
   // Buffer byte ranges and offsets must fit in 32 bits (with room for the
   // out-of-range sentinel), and the grid in an int.
   const int64_t lim = (int64_t)0xFFFFF000u;

@@ -63,6 +63,12 @@ Path forced_path() {
   return P_AUTO;
 }
 
+// OBL_GEMM set (tests forcing a GEMM kernel): keep stage 2 on the fp32 workspace.
+bool gemm_forced_any() {
+  const char* e = std::getenv("OBL_GEMM");
+  return e && e[0];
+}
+
 Path choose_path(int64_t M, obl_status* st) {
   Path p = forced_path();
   if (p == P_AUTO) {
@@ -250,11 +256,28 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
     // Stage 1: T1 = ((X ⊙ b) S2^T) ⊙ m, kept in fp32 in the workspace.
     LinearArgs s1{X, x_dtype, M, K, S2_packed, Kmid, b, m, scale_dtype, workspace, OBL_F32,
                   (hipStream_t)stream};
-    st = run_linear(s1, path);
-    if (st != OBL_OK) return st;
     // Stage 2: Y = (T1 S1^T) ⊙ a (no input-side scale).
     LinearArgs s2{workspace, OBL_F32, M, Kmid, S1_packed, N, nullptr, a, scale_dtype, Y, y_dtype,
                   (hipStream_t)stream};
+    // Prefill: the GEMM rounds T1 to bf16 for stage 2 anyway (one rounding of
+    // the input-side operand), so stage 1 also writes that bf16 copy into
+    // library scratch and stage 2 reads it with the bf16 prefill kernel.
+    if (path == P_GEMM && !gemm_forced_any() && x_dtype == OBL_BF16 &&
+        gemm_wide_shape_ok(M, K, Kmid, true, X, S2_packed)) {
+      DeviceInfo dev;
+      if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+      Scratch sc{};
+      const size_t floats = (size_t)((M * Kmid + 1) / 2 + 64);
+      if (scratch_reserve(dev.device, floats, &sc) != hipSuccess) return OBL_ERR_HIP;
+      void* t1b = sc.partials;                      // hipMalloc'ed: 256-byte aligned
+      if (gemm_wide_shape_ok(M, Kmid, N, false, t1b, S1_packed)) {
+        s1.Y2 = t1b;
+        s2.X = t1b;
+        s2.x_dtype = OBL_BF16;
+      }
+    }
+    st = run_linear(s1, path);
+    if (st != OBL_OK) return st;
     return run_linear(s2, path);
   } catch (...) {
     return OBL_ERR_INTERNAL;

@@ -19,6 +19,7 @@ struct LinearArgs {
   void* Y;            // [M][N]
   int y_dtype;        // DT_F32 or DT_BF16
   hipStream_t stream;
+  void* Y2 = nullptr; // optional bf16 copy of Y (prefill GEMM only; see gemm_wide_eligible)
 };
 
 struct DeviceInfo {
@@ -42,6 +43,8 @@ hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
 // Main prefill kernel (bf16 activations); launch_gemm_mfma dispatches to it.
 bool gemm_wide_eligible(const LinearArgs& a);
+// Shape/alignment test for a bf16-activation prefill call of the given sizes.
+bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const void* X, const void* W);
 hipError_t launch_gemm_wide(const LinearArgs& a, const DeviceInfo& dev);
 
 // Largest M served by the LUT GEMV and by the decode kernel.

@@ -313,6 +313,28 @@ def test_dbf_prefill(M):
     assert r1 <= G.TOL_GEMM and r <= G.TOL_DBF_GEMM
 
 
+@pytest.mark.parametrize("Kmid", [2048, 3072, 4736])
+def test_dbf_prefill_full_size(Kmid):
+    """DBF prefill at M = 512 with K = N = 4096 and Kmid for 1.0 / 1.5 / 2.3 sign
+    bits per weight (DBF page, "Belangrijkste Bijdragen": the middle dimension
+    sets the ratio).  Sampled rows against the oracle, stage 1 and composed."""
+    M = 512
+    G.say(f"dbf prefill M={M} Kmid={Kmid}")
+    c = WL.dbf_case(M, 4096, Kmid, 4096, seed=Kmid)
+    X = G.dev(c.X, "bf16")
+    S2p = B.pack_signs(G.signs_dev(c.S2))
+    S1p = B.pack_signs(G.signs_dev(c.S1))
+    b, m, a = (G.dev(v, "f16") for v in (c.b, c.m, c.a))
+    Y, T1 = B.dbf_linear(X, S2p, S1p, b, m, a, out_dtype=torch.bfloat16)
+    rows = np.unique(np.concatenate([np.random.default_rng(Kmid).choice(M, 20, replace=False), [0, M - 1]]))
+    r1 = O.max_normalised_error(G.host64(T1)[rows], O.dbf_stage1(c.X[rows], c.S2, c.b, c.m),
+                                O.onebit_error_scale(c.X[rows], c.m, c.b))
+    r = O.max_normalised_error(G.host64(Y)[rows], O.dbf_linear(c.X[rows], c.S1, c.S2, c.a, c.m, c.b),
+                               O.dbf_error_scale(c.X[rows], c.b, c.m, c.a))
+    G.say(f"  stage1 {r1:.3e} composed {r:.3e}")
+    assert r1 <= G.TOL_GEMM and r <= G.TOL_DBF_GEMM
+
+
 # ------------------------------------------------------------------ determinism, edge cases
 @pytest.mark.parametrize("path,M", [("lut", 1), ("decode", 16), ("gemm", 256)])
 def test_bitwise_reproducible(path, M):
