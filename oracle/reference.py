@@ -50,6 +50,9 @@ __all__ = [
     "rank1_power",
     "svid",
     "max_normalised_error",
+    "transpose_signs",
+    "onebit_backward",
+    "backward_error_scales",
 ]
 
 
@@ -196,6 +199,54 @@ def dbf_error_scale(X, b, m, a) -> np.ndarray:
     X = _f64(X)
     base = np.abs(X) @ np.abs(_f64(b))
     return base[:, None] * np.abs(_f64(m)).sum() * np.abs(_f64(a))[None, :]
+
+
+# --------------------------------------------------------------------------
+# Backward of the OneBit layer (OneBit page, "知识蒸馏": the layer
+# Y = [(X ⊙ g) W_±1^T] ⊙ h is trained by distillation, so its input and scale
+# gradients are needed; they follow from the plain definition by the chain rule.)
+# --------------------------------------------------------------------------
+def transpose_signs(P, rows: int, K: int) -> np.ndarray:
+    """Packed signs of the transposed sign matrix: ``P^T`` [K, rows/32] from
+    ``P`` [rows, K/32] (same packing format, now along the ``rows`` axis)."""
+    return pack_signs(unpack_signs(P, K).T)
+
+
+def onebit_backward(X, W_sign, a, b, dY):
+    """Gradients of ``Y = X W^T`` with ``W = W_sign ⊙ (a b^T)`` for an upstream
+    gradient ``dY`` [M, N]: returns ``(dX, da, db)``.
+
+    ``dX = dY W``; with ``dW = dY^T X`` the scale gradients are
+    ``da_j = Σ_k dW_jk s_jk b_k`` and ``db_k = Σ_j dW_jk s_jk a_j`` (the signs
+    themselves are fixed and get no gradient).
+    """
+    X = _f64(X)
+    dY = _f64(dY)
+    S = _f64(W_sign)
+    a = _f64(a)
+    b = _f64(b)
+    W = onebit_dense_weight(S, a, b)
+    dX = dY @ W
+    dW = dY.T @ X
+    da = (dW * S * b[None, :]).sum(axis=1)
+    db = (dW * S * a[:, None]).sum(axis=0)
+    return dX, da, db
+
+
+def backward_error_scales(X, a, b, dY):
+    """Normalising scales bounding every partial sum of each gradient:
+    ``S_dX[i, k] = |b_k| Σ_j |dY_ij a_j|``, ``S_da[j] = Σ_i |dY_ij| Σ_k |x_ik b_k|``,
+    ``S_db[k] = Σ_i |x_ik| Σ_j |dY_ij a_j|``."""
+    X = _f64(X)
+    dY = _f64(dY)
+    a = np.abs(_f64(a))
+    b = np.abs(_f64(b))
+    ga = np.abs(dY) @ a                    # [M]: Σ_j |dY_ij a_j|
+    xb = np.abs(X) @ b                     # [M]: Σ_k |x_ik b_k|
+    s_dx = ga[:, None] * b[None, :]
+    s_da = np.abs(dY).T @ xb
+    s_db = np.abs(X).T @ ga
+    return s_dx, s_da, s_db
 
 
 # --------------------------------------------------------------------------

@@ -263,6 +263,72 @@ def pin_dbf_bruteforce(dbf_linear, seed=29):
 DBF_PINS = (pin_dbf_chain, pin_dbf_hadamard, pin_dbf_int_exact, pin_dbf_bruteforce)
 
 
+def pin_backward_finite_differences(onebit_backward, seed=31):
+    """The gradients of L = Σ_ij Y_ij dY_ij (Y the OneBit layer) by central
+    differences in fp64 (step 1e-6, error O(h^2) plus rounding) must match
+    dX, da and db."""
+    import oracle as O
+    rng = np.random.default_rng(seed)
+    M, K, N = 3, 64, 32
+    X = rng.standard_normal((M, K))
+    S = random_signs(rng, (N, K))
+    a = rng.standard_normal(N)
+    b = rng.standard_normal(K)
+    dY = rng.standard_normal((M, N))
+    dX, da, db = onebit_backward(X, S, a, b, dY)
+
+    def L(X_, a_, b_):
+        return float((O.onebit_linear(X_, S, a_, b_) * dY).sum())
+
+    h = 1e-6
+    errs = []
+    for name, base, grad, f in (("dX", X, dX, lambda v: L(v, a, b)),
+                                ("da", a, da, lambda v: L(X, v, b)),
+                                ("db", b, db, lambda v: L(X, a, v))):
+        g = np.asarray(grad, float)
+        if g.shape != base.shape:
+            errs.append(f"{name} shape {g.shape} != {base.shape}")
+            continue
+        flat = base.reshape(-1)
+        for i in range(0, flat.size, max(1, flat.size // 24)):
+            e = np.zeros_like(flat)
+            e[i] = h
+            num = (f((flat + e).reshape(base.shape)) - f((flat - e).reshape(base.shape))) / (2 * h)
+            if abs(num - g.reshape(-1)[i]) > 1e-6 * (1 + abs(num)):
+                errs.append(f"{name}[{i}] {g.reshape(-1)[i]} vs finite difference {num}")
+    return errs
+
+
+def pin_backward_bruteforce(onebit_backward, seed=37):
+    """Pure-Python loops at M=2, K=8, N=4 over the chain-rule sums."""
+    rng = np.random.default_rng(seed)
+    M, K, N = 2, 8, 4
+    X = rng.standard_normal((M, K))
+    S = random_signs(rng, (N, K))
+    a = rng.standard_normal(N)
+    b = rng.standard_normal(K)
+    dY = rng.standard_normal((M, N))
+    dX, da, db = onebit_backward(X, S, a, b, dY)
+    errs = []
+    for i in range(M):
+        for k in range(K):
+            ref = sum(float(dY[i, j]) * int(S[j, k]) * float(a[j]) * float(b[k]) for j in range(N))
+            if abs(dX[i, k] - ref) > 1e-13 * (1 + abs(ref)):
+                errs.append(f"dX ({i},{k})")
+    for j in range(N):
+        ref = sum(float(dY[i, j]) * float(X[i, k]) * int(S[j, k]) * float(b[k]) for i in range(M) for k in range(K))
+        if abs(da[j] - ref) > 1e-13 * (1 + abs(ref)):
+            errs.append(f"da ({j})")
+    for k in range(K):
+        ref = sum(float(dY[i, j]) * float(X[i, k]) * int(S[j, k]) * float(a[j]) for i in range(M) for j in range(N))
+        if abs(db[k] - ref) > 1e-13 * (1 + abs(ref)):
+            errs.append(f"db ({k})")
+    return errs
+
+
+BACKWARD_PINS = (pin_backward_finite_differences, pin_backward_bruteforce)
+
+
 def run(pins, *fns):
     out = []
     for p in pins:

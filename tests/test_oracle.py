@@ -181,3 +181,55 @@ DBF_MUTANTS = {
 @pytest.mark.parametrize("name", sorted(DBF_MUTANTS))
 def test_dbf_mutants_fail_some_pin(name):
     assert P.run(P.DBF_PINS, DBF_MUTANTS[name]) != [], f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------- backward and transposed packing
+@pytest.mark.parametrize("pin", P.BACKWARD_PINS, ids=lambda p: p.__name__)
+def test_backward_pins(pin):
+    assert pin(O.onebit_backward) == []
+
+
+def test_transpose_signs_is_the_transposed_packing():
+    rng = np.random.default_rng(41)
+    S = W.random_signs(rng, (96, 160))
+    P_ = O.pack_signs(S)
+    PT = O.transpose_signs(P_, 96, 160)
+    assert PT.shape == (160, 3) and PT.dtype == np.uint32
+    assert np.array_equal(O.unpack_signs(PT, 96), S.T)
+    # bit j of PT[k, w] is the sign of S[32w + j, k]
+    k, w, j = 7, 2, 5
+    assert ((int(PT[k, w]) >> j) & 1) == (1 if S[32 * w + j, k] < 0 else 0)
+    assert np.array_equal(O.transpose_signs(PT, 160, 96), P_)
+
+
+def test_backward_error_scales_bound_gradients():
+    rng = np.random.default_rng(43)
+    X, dY = rng.standard_normal((4, 64)), rng.standard_normal((4, 32))
+    S = W.random_signs(rng, (32, 64))
+    a, b = rng.standard_normal(32), rng.standard_normal(64)
+    dX, da, db = O.onebit_backward(X, S, a, b, dY)
+    sdx, sda, sdb = O.backward_error_scales(X, a, b, dY)
+    assert np.all(np.abs(dX) <= sdx + 1e-12) and np.all(np.abs(da) <= sda + 1e-12)
+    assert np.all(np.abs(db) <= sdb + 1e-12)
+
+
+def _bw(X, S, a, b, dY, **over):
+    args = dict(a=a, b=b)
+    args.update(over)
+    return O.onebit_backward(X, S, args["a"], args["b"], dY)
+
+
+BACKWARD_MUTANTS = {
+    "dX_without_scales": lambda X, S, a, b, dY: (np.asarray(dY, float) @ np.asarray(S, float),
+                                                 *_bw(X, S, a, b, dY)[1:]),
+    "dX_missing_b": lambda X, S, a, b, dY: (_bw(X, S, a, b, dY, b=np.ones(len(b)))[0], *_bw(X, S, a, b, dY)[1:]),
+    "da_missing_b": lambda X, S, a, b, dY: (_bw(X, S, a, b, dY)[0], _bw(X, S, a, b, dY, b=np.ones(len(b)))[1],
+                                            _bw(X, S, a, b, dY)[2]),
+    "db_missing_a": lambda X, S, a, b, dY: (*_bw(X, S, a, b, dY)[:2], _bw(X, S, a, b, dY, a=np.ones(len(a)))[2]),
+    "sign_flip": lambda X, S, a, b, dY: O.onebit_backward(X, -np.asarray(S), a, b, dY),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutants_fail_some_pin(name):
+    assert P.run(P.BACKWARD_PINS, BACKWARD_MUTANTS[name]) != [], f"mutant {name} passed every pin"
