@@ -177,6 +177,34 @@ def dbf_prefill_setup(torch, B, WL, O, M=512, K=4096, Kmid=3072, N=4096, copies=
     return c, launches, err, copies
 
 
+def backward_setup(torch, B, WL, O, M, K, N, copies):
+    """Backward of the layer (dX, da, db) on synthetic dY; parity on sampled rows
+    of dX and on da, db (full, the oracle is a dense fp64 product)."""
+    import numpy as np
+    rng = np.random.default_rng(M + K + N)
+    X = WL.round_to(rng.standard_normal((M, K)), "bf16")
+    dY = WL.round_to(rng.standard_normal((M, N)), "bf16")
+    S = WL.random_signs(rng, (N, K))
+    a = WL.round_to(np.abs(rng.standard_normal(N)) * 0.02 + 1e-3, "f16")
+    b = WL.round_to(np.abs(rng.standard_normal(K)) * 0.02 + 1e-3, "f16")
+    dev = torch.device("cuda")
+    t = lambda v, dt: torch.from_numpy(v).to(torch.float32).to(dt).to(dev)
+    Xd, dYd, ad, bd = t(X, torch.bfloat16), t(dY, torch.bfloat16), t(a, torch.float16), t(b, torch.float16)
+    W = B.pack_signs(torch.from_numpy(S).to(dev))
+    Wt = B.transpose_signs(W, N, K)
+    ws = torch.empty(M * (N + K), dtype=torch.float32, device=dev)
+    dX, da, db, _ = B.linear_backward(dYd, Xd, W, Wt, ad, bd, workspace=ws)
+    torch.cuda.synchronize()
+    rdX, rda, rdb = O.onebit_backward(X, S, a, b, dY)
+    sdx, sda, sdb = O.backward_error_scales(X, a, b, dY)
+    err = max(O.max_normalised_error(dX.float().cpu().numpy().astype(np.float64), rdX, sdx),
+              O.max_normalised_error(da.cpu().numpy().astype(np.float64), rda, sda),
+              O.max_normalised_error(db.cpu().numpy().astype(np.float64), rdb, sdb))
+    reps = [(W, Wt)] + [(W.clone(), Wt.clone()) for _ in range(copies - 1)]
+    launches = [(lambda w=w, wt=wt: B.linear_backward(dYd, Xd, w, wt, ad, bd, workspace=ws)) for (w, wt) in reps]
+    return launches, err
+
+
 def cpu_baseline(WL, O, budget_s: float = 12.0):
     """Time the fp64 oracle on workload 2 (the headline) for a bounded sample."""
     import numpy as np
@@ -319,6 +347,17 @@ def main():
                         "parity_max_normalised_error_sampled": float(f"{e6:.3e}"), "copies": R6}
         log(f"[bench] {c6.name}: {ms6 * 1e3:.1f} us per call, {tf6:.1f} TFLOP/s")
         del l6, t6
+        # backward of the layer at the batched-decode shape (two sign contractions + reductions)
+        l7, e7 = backward_setup(torch, B, WL, O, 16, 4096, 4096, copies=64)
+        assert e7 <= 1e-5, "parity failed on the backward"
+        t7 = Timed(torch, l7)
+        _, ms7 = t7.run(args.warmup, args.steps)
+        sec["backward-16x4096x4096"] = {"us_per_call": round(ms7 * 1e3, 3),
+                                        "weight_GBps": round(2 * 4096 * 4096 / 8 / (ms7 * 1e-3) / 1e9, 1),
+                                        "parity_max_normalised_error": float(f"{e7:.3e}"), "copies": 64,
+                                        "note": "weight bytes counted twice: W and its transposed packing"}
+        log(f"[bench] backward-16x4096x4096: {ms7 * 1e3:.2f} us per call")
+        del l7, t7
         out["secondary"] = sec
 
     if args.copy_calibration_mib > 0:

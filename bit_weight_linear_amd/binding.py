@@ -27,7 +27,8 @@ OBL_OK, OBL_ERR_NULL, OBL_ERR_SHAPE, OBL_ERR_DTYPE, OBL_ERR_ALIGN, OBL_ERR_ALIAS
 # obl_dtype codes
 OBL_F32, OBL_F16, OBL_BF16, OBL_I8 = range(4)
 
-EXPORTS = ("obl_pack_signs", "obl_linear", "dbf_linear", "obl_status_string", "obl_version")
+EXPORTS = ("obl_pack_signs", "obl_linear", "dbf_linear", "obl_transpose_signs", "obl_linear_backward",
+           "obl_status_string", "obl_version")
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 lib.obl_pack_signs.argtypes = [_vp, _int, _i64, _i64, _vp, _vp]
@@ -37,6 +38,11 @@ lib.obl_linear.restype = _int
 lib.dbf_linear.argtypes = [_vp, _int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _int,
                            _vp, _vp, _int, _vp]
 lib.dbf_linear.restype = _int
+lib.obl_transpose_signs.argtypes = [_vp, _i64, _i64, _vp, _vp]
+lib.obl_transpose_signs.restype = _int
+lib.obl_linear_backward.argtypes = [_vp, _vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _int,
+                                    _vp, _int, _vp, _vp, _vp, _vp]
+lib.obl_linear_backward.restype = _int
 lib.obl_status_string.argtypes = [_int]
 lib.obl_status_string.restype = ctypes.c_char_p
 lib.obl_version.argtypes = []
@@ -123,3 +129,34 @@ def dbf_linear(X: torch.Tensor, S2_packed: torch.Tensor, S1_packed: torch.Tensor
                           _ptr(b), _ptr(m), _ptr(a), dtype_code(a.dtype), _ptr(workspace), _ptr(out),
                           dtype_code(out.dtype), _stream(X)), "dbf_linear")
     return out, workspace
+
+
+def transpose_signs(P: torch.Tensor, rows: int, K: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed signs of the transposed matrix: [K, rows/32] from [rows, K/32]."""
+    _dev(P, "P")
+    if out is None:
+        out = torch.empty((K, rows // 32), dtype=torch.int32, device=P.device)
+    _check(lib.obl_transpose_signs(_ptr(P), rows, K, _ptr(out), _stream(P)), "obl_transpose_signs")
+    return out
+
+
+def linear_backward(dY: torch.Tensor, X: torch.Tensor, W_packed: torch.Tensor, Wt_packed: torch.Tensor,
+                    a: torch.Tensor, b: torch.Tensor, dx_dtype: torch.dtype = torch.float32,
+                    workspace: Optional[torch.Tensor] = None):
+    """(dX, da, db) of Y = ((X ⊙ b) W_sign^T) ⊙ a for the upstream gradient dY,
+    through ``obl_linear_backward``.  Returns (dX, da, db, workspace); the
+    flat fp32 workspace holds T = (X ⊙ b) W_sign^T [M][N], then U = (dY ⊙ a) W_sign [M][K]."""
+    for t, n in ((dY, "dY"), (X, "X"), (W_packed, "W_packed"), (Wt_packed, "Wt_packed"), (a, "a"), (b, "b")):
+        _dev(t, n)
+    M, K = X.shape
+    N = W_packed.shape[0]
+    if workspace is None:
+        workspace = torch.empty(M * (N + K), dtype=torch.float32, device=X.device)
+    dX = torch.empty((M, K), dtype=dx_dtype, device=X.device)
+    da = torch.empty(N, dtype=torch.float32, device=X.device)
+    db = torch.empty(K, dtype=torch.float32, device=X.device)
+    _check(lib.obl_linear_backward(_ptr(dY), _ptr(X), dtype_code(X.dtype), M, K, _ptr(W_packed), _ptr(Wt_packed),
+                                   N, _ptr(a), _ptr(b), dtype_code(a.dtype), _ptr(dX), dtype_code(dx_dtype),
+                                   _ptr(da), _ptr(db), _ptr(workspace), _stream(X)),
+           "obl_linear_backward")
+    return dX, da, db, workspace

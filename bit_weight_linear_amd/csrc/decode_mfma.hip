@@ -183,7 +183,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_mfma_kernel(
     b1 = to_f32(pre[kc + 1]);
     if (k >= K) b0 = b1 = 0.f;
   }
-  const float post_c = to_f32(post[min(n0 + 16 * wave + j, N - 1)]);
+  const float post_c = (post ? to_f32(post[min(n0 + 16 * wave + j, N - 1)]) : 1.f);
 
   // ---- 4. Remaining LDS writes, then one barrier.
   if constexpr (MODE != MODE_S3 && !FAST) {
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= MN) return;
   const int64_t n = e % N;
-  const float s = to_f32(post[n]);
+  const float s = (post ? to_f32(post[n]) : 1.f);
   float acc = 0.f;
   int sl = 0;
   for (; sl + 8 <= nslices; sl += 8) {

@@ -200,7 +200,7 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   dma(xb, wb, min(1, nk - 1));
 
   // Output scales of this tile, while stages 0 and 1 are in flight.
-  for (int c = tid; c < GW_BN; c += GW_THREADS) post_s[c] = to_f32(post[min(bn0 + c, N - 1)]);
+  for (int c = tid; c < GW_BN; c += GW_THREADS) post_s[c] = (post ? to_f32(post[min(bn0 + c, N - 1)]) : 1.f);
   __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): stages 0 and 1 landed
   __syncthreads();
 

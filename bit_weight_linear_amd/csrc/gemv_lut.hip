@@ -91,7 +91,7 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
 #pragma unroll
   for (int r = 0; r < RPH; ++r) {
     const int row = hw + LUT_HALFWAVES * r;
-    post_r[r] = to_f32(post[row0 + (row < nrows ? row : nrows - 1)]);
+    post_r[r] = (post ? to_f32(post[row0 + (row < nrows ? row : nrows - 1)]) : 1.f);
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
   }

@@ -220,6 +220,85 @@ obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
   }
 }
 
+obl_status obl_transpose_signs(const uint32_t* packed, int64_t rows, int64_t K, uint32_t* packed_t,
+                               void* stream) {
+  try {
+    if (!packed || !packed_t) return OBL_ERR_NULL;
+    if (rows < 1 || K < 1 || K % 32 != 0 || rows % 32 != 0) return OBL_ERR_SHAPE;
+    int64_t pb = checked_bytes(rows, K / 32, 4), tb = checked_bytes(K, rows / 32, 4);
+    if (pb < 0 || tb < 0) return OBL_ERR_SHAPE;
+    if (!aligned(packed, 4) || !aligned(packed_t, 4)) return OBL_ERR_ALIGN;
+    if (overlap(range_of(packed, pb), range_of(packed_t, tb))) return OBL_ERR_ALIAS;
+    hipError_t e = launch_transpose_signs(packed, rows, K, packed_t, (hipStream_t)stream);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+    return OBL_OK;
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
+obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                               const uint32_t* W_packed, const uint32_t* Wt_packed, int64_t N,
+                               const void* a, const void* b, obl_dtype scale_dtype,
+                               void* dX, obl_dtype dx_dtype, float* da, float* db,
+                               float* workspace, void* stream) {
+  try {
+    if (M < 0 || K < 1 || N < 1 || K % 32 != 0 || N % 32 != 0) return OBL_ERR_SHAPE;
+    if (!W_packed || !Wt_packed || !a || !b || !da || !db) return OBL_ERR_NULL;
+    if (M > 0 && (!dY || !X || !dX || !workspace)) return OBL_ERR_NULL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(dx_dtype))
+      return OBL_ERR_DTYPE;
+    if (!linear_dtypes_ok(x_dtype, scale_dtype, dx_dtype)) return OBL_ERR_DTYPE;
+    const int xs = elem_size(x_dtype), ss = elem_size(scale_dtype), ds = elem_size(dx_dtype);
+    int64_t gyb = checked_bytes(M, N, xs), xb = checked_bytes(M, K, xs);
+    int64_t wb = checked_bytes(N, K / 32, 4), wtb = checked_bytes(K, N / 32, 4);
+    int64_t ab = checked_bytes(N, 1, ss), bb = checked_bytes(K, 1, ss);
+    int64_t dxb = checked_bytes(M, K, ds), dab = checked_bytes(N, 1, 4), dbb = checked_bytes(K, 1, 4);
+    int64_t wsb = checked_bytes(M, N + K, 4);
+    if (gyb < 0 || xb < 0 || wb < 0 || wtb < 0 || ab < 0 || bb < 0 || dxb < 0 || dab < 0 || dbb < 0 ||
+        wsb < 0)
+      return OBL_ERR_SHAPE;
+    if ((M > 0 && (!aligned(dY, xs) || !aligned(X, xs) || !aligned(dX, ds) || !aligned(workspace, 4))) ||
+        !aligned(W_packed, 4) || !aligned(Wt_packed, 4) || !aligned(a, ss) || !aligned(b, ss) ||
+        !aligned(da, 4) || !aligned(db, 4))
+      return OBL_ERR_ALIGN;
+    const Range ins[6] = {range_of(dY, gyb), range_of(X, xb), range_of(W_packed, wb),
+                          range_of(Wt_packed, wtb), range_of(a, ab), range_of(b, bb)};
+    const Range outs[4] = {range_of(dX, dxb), range_of(da, dab), range_of(db, dbb), range_of(workspace, wsb)};
+    for (int o = 0; o < 4; ++o) {
+      for (const Range& r : ins)
+        if (overlap(outs[o], r)) return OBL_ERR_ALIAS;
+      for (int p = o + 1; p < 4; ++p)
+        if (overlap(outs[o], outs[p])) return OBL_ERR_ALIAS;
+    }
+    obl_status st = OBL_OK;
+    Path path = choose_path(M, &st);
+    if (st != OBL_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    if (M == 0) {
+      // Empty batch: the reduction kernel writes the zero sums da = db = 0.
+      hipError_t e = launch_backward_grads(x_dtype, scale_dtype, dx_dtype, dY, X, nullptr, nullptr, b, 0, K,
+                                           N, dX, da, db, hs);
+      return (e != hipSuccess || hipGetLastError() != hipSuccess) ? OBL_ERR_HIP : OBL_OK;
+    }
+    float* T = workspace;                 // [M][N]
+    float* U = workspace + M * N;         // [M][K]
+    // T = (X ⊙ b^T) W_sign^T and U = (dY ⊙ a^T) W_sign, both without an output scale.
+    LinearArgs t{X, x_dtype, M, K, W_packed, N, b, nullptr, scale_dtype, T, OBL_F32, hs};
+    st = run_linear(t, path);
+    if (st != OBL_OK) return st;
+    LinearArgs u{dY, x_dtype, M, N, Wt_packed, K, a, nullptr, scale_dtype, U, OBL_F32, hs};
+    st = run_linear(u, path);
+    if (st != OBL_OK) return st;
+    hipError_t e = launch_backward_grads(x_dtype, scale_dtype, dx_dtype, dY, X, T, U, b, M, K, N, dX, da,
+                                         db, hs);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+    return OBL_OK;
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
 obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const uint32_t* S2_packed, int64_t Kmid,
                       const uint32_t* S1_packed, int64_t N,

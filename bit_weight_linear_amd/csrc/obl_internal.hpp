@@ -14,7 +14,7 @@ struct LinearArgs {
   const uint32_t* W;  // [N][K/32] packed signs
   int64_t N;
   const void* pre;    // [K] or nullptr (= all ones)
-  const void* post;   // [N]
+  const void* post;   // [N], or nullptr (= all ones; internal calls only)
   int scale_dtype;    // DT_F32 or DT_F16
   void* Y;            // [M][N]
   int y_dtype;        // DT_F32 or DT_BF16
@@ -39,6 +39,10 @@ hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out);
 hipError_t launch_pack_signs(const void* S, int s_dtype, int64_t rows, int64_t K, uint32_t* P,
                              hipStream_t stream);
 hipError_t launch_gemv_lut(const LinearArgs& a, const DeviceInfo& dev);
+hipError_t launch_transpose_signs(const uint32_t* P, int64_t rows, int64_t K, uint32_t* PT, hipStream_t st);
+hipError_t launch_backward_grads(int x_dtype, int scale_dtype, int dx_dtype, const void* dY, const void* X,
+                                 const float* T, const float* U, const void* b, int64_t M, int64_t K,
+                                 int64_t N, void* dX, float* da, float* db, hipStream_t st);
 hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
 // Main prefill kernel (bf16 activations); launch_gemm_mfma dispatches to it.

@@ -125,6 +125,44 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const void* b, const void* m, const void* a, obl_dtype scale_dtype,
                       float* workspace, void* Y, obl_dtype y_dtype, void* stream);
 
+/*
+ * obl_transpose_signs -- packed signs of the transposed sign matrix.
+ *   packed    [rows][K/32] packed signs (format above).
+ *   packed_t  [K][rows/32], written: bit j of packed_t[k][w] is the sign of
+ *             row 32*w + j, column k (the same format, packed along rows).
+ *   Needed once per weight by obl_linear_backward, whose input gradient
+ *   contracts over the output dimension (OneBit page, knowledge-distillation
+ *   block: the layer is trained through its gradients).
+ *   Errors: OBL_ERR_NULL, OBL_ERR_SHAPE (rows or K < 1, or not multiples of
+ *           32), OBL_ERR_ALIGN (4-byte), OBL_ERR_ALIAS, OBL_ERR_HIP.
+ */
+obl_status obl_transpose_signs(const uint32_t* packed, int64_t rows, int64_t K, uint32_t* packed_t,
+                               void* stream);
+
+/*
+ * obl_linear_backward -- gradients of Y = ((X ⊙ b) W_sign^T) ⊙ a for an
+ * upstream gradient dY [M][N] (OneBit page, knowledge-distillation block; the
+ * formulas are the chain rule on proposition 1's right-hand side):
+ *   dX = ((dY ⊙ a) · W_sign) ⊙ b          [M][K], dx_dtype (OBL_F32 / OBL_BF16)
+ *   da_j = Σ_i dY_ij · T_ij,  T = (X ⊙ b) W_sign^T      [N] fp32
+ *   db_k = Σ_i x_ik · U_ik,   U = (dY ⊙ a) W_sign       [K] fp32
+ *   dY, X      x_dtype (OBL_F32 or OBL_BF16), row-major [M][N] and [M][K].
+ *   W_packed   [N][K/32]; Wt_packed [K][N/32] from obl_transpose_signs.
+ *   a [N], b [K] scale_dtype (OBL_F32 or OBL_F16).
+ *   workspace  fp32 [M][N + K], caller-owned: after completion it holds T
+ *              then U.  Must not overlap any other argument.
+ *   Arithmetic: T and U follow obl_linear's rules for the same M (the decode
+ *   paths keep fp32 accuracy, the prefill path rounds one input-side factor
+ *   to bf16); the sums over M are fp32 in a fixed order (reproducible).
+ *   M = 0 writes da = db = 0.
+ *   Errors: as obl_linear; N must also be a multiple of 32.
+ */
+obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                               const uint32_t* W_packed, const uint32_t* Wt_packed, int64_t N,
+                               const void* a, const void* b, obl_dtype scale_dtype,
+                               void* dX, obl_dtype dx_dtype, float* da, float* db,
+                               float* workspace, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* obl_status_string(obl_status status);
 

@@ -135,3 +135,43 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         b.pack_signs(torch.ones((2, 32), dtype=torch.int8))
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 64, 64, W), b.OBL_ERR_NULL),
+    ((X, 64, 64, None), b.OBL_ERR_NULL),
+    ((X, 48, 64, W), b.OBL_ERR_SHAPE),          # rows not a multiple of 32
+    ((X, 64, 40, W), b.OBL_ERR_SHAPE),
+    ((X, 0, 64, W), b.OBL_ERR_SHAPE),
+    ((P(0x10_0000_0002), 64, 64, W), b.OBL_ERR_ALIGN),
+    ((X, 64, 64, P(0x10_0000_0000 + 32)), b.OBL_ERR_ALIAS),
+])
+def test_transpose_rejects(args, code):
+    assert L.obl_transpose_signs(*args, None) == code
+
+
+# obl_linear_backward(dY, X, xd, M, K, W, Wt, N, a, b, sd, dX, dxd, da, db, ws, stream)
+GY, WT, DX, DA, DB = (P(0x90_0000_0000 + 0x10_0000_0000 * i) for i in range(5))
+
+
+def bwd(dY=GY, X_=X, xd=b.OBL_BF16, M=4, K=4096, W_=W, Wt=WT, N=4096, a=A, bb=B_, sd=b.OBL_F16,
+        dX=DX, dxd=b.OBL_F32, da=DA, db=DB, ws=WS):
+    return L.obl_linear_backward(dY, X_, xd, M, K, W_, Wt, N, a, bb, sd, dX, dxd, da, db, ws, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Wt=None), b.OBL_ERR_NULL),
+    (dict(da=None), b.OBL_ERR_NULL),
+    (dict(ws=None), b.OBL_ERR_NULL),
+    (dict(N=4016), b.OBL_ERR_SHAPE),            # N must be a multiple of 32 (contraction of dX)
+    (dict(K=4016), b.OBL_ERR_SHAPE),
+    (dict(M=-1), b.OBL_ERR_SHAPE),
+    (dict(xd=b.OBL_F16), b.OBL_ERR_DTYPE),
+    (dict(dxd=b.OBL_I8), b.OBL_ERR_DTYPE),
+    (dict(da=P(0xB0_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(dX=P(0x10_0000_0000 + 64)), b.OBL_ERR_ALIAS),     # dX inside X
+    (dict(db=DA), b.OBL_ERR_ALIAS),                          # two outputs overlap
+    (dict(ws=GY), b.OBL_ERR_ALIAS),                          # workspace == dY
+])
+def test_backward_rejects(kw, code):
+    assert bwd(**kw) == code
