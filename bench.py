@@ -358,6 +358,23 @@ def main():
                                         "note": "weight bytes counted twice: W and its transposed packing"}
         log(f"[bench] backward-16x4096x4096: {ms7 * 1e3:.2f} us per call")
         del l7, t7
+        # SVID conversion of the headline layer's dense fp16 weight (32 power iterations)
+        rng8 = np.random.default_rng(8)
+        Wd = torch.from_numpy(WL.round_to(rng8.standard_normal((11008, 4096)) * 0.02, "f16")).to(torch.float16).cuda()
+        P8, a8, b8 = B.svid(Wd, iters=32)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(3):
+            B.svid(Wd, iters=32)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms8 = ev0.elapsed_time(ev1) / 3
+        passes = 2 * 32 + 2                      # |W| reads: two per iteration, the final row pass, Sign(W)
+        sec["svid-11008x4096-f16-32iters"] = {"ms_per_conversion": round(ms8, 3),
+                                              "weight_read_GBps": round(passes * Wd.numel() * 2 / (ms8 * 1e-3) / 1e9, 1)}
+        log(f"[bench] svid-11008x4096-f16-32iters: {ms8:.3f} ms per conversion")
+        del Wd, P8, a8, b8
         out["secondary"] = sec
 
     if args.copy_calibration_mib > 0:

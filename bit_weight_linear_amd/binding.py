@@ -28,7 +28,7 @@ OBL_OK, OBL_ERR_NULL, OBL_ERR_SHAPE, OBL_ERR_DTYPE, OBL_ERR_ALIGN, OBL_ERR_ALIAS
 OBL_F32, OBL_F16, OBL_BF16, OBL_I8 = range(4)
 
 EXPORTS = ("obl_pack_signs", "obl_linear", "dbf_linear", "obl_transpose_signs", "obl_linear_backward",
-           "obl_status_string", "obl_version")
+           "obl_svid", "obl_status_string", "obl_version")
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 lib.obl_pack_signs.argtypes = [_vp, _int, _i64, _i64, _vp, _vp]
@@ -43,6 +43,8 @@ lib.obl_transpose_signs.restype = _int
 lib.obl_linear_backward.argtypes = [_vp, _vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _int,
                                     _vp, _int, _vp, _vp, _vp, _vp]
 lib.obl_linear_backward.restype = _int
+lib.obl_svid.argtypes = [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _int, _vp]
+lib.obl_svid.restype = _int
 lib.obl_status_string.argtypes = [_int]
 lib.obl_status_string.restype = ctypes.c_char_p
 lib.obl_version.argtypes = []
@@ -160,3 +162,15 @@ def linear_backward(dY: torch.Tensor, X: torch.Tensor, W_packed: torch.Tensor, W
                                    _ptr(da), _ptr(db), _ptr(workspace), _stream(X)),
            "obl_linear_backward")
     return dX, da, db, workspace
+
+
+def svid(W: torch.Tensor, iters: int = 32, scale_dtype: torch.dtype = torch.float16):
+    """(packed Sign(W), a, b) with a b^T the rank-1 approximation of |W|, through ``obl_svid``."""
+    _dev(W, "W")
+    N, K = W.shape
+    packed = torch.empty((N, K // 32), dtype=torch.int32, device=W.device)
+    a = torch.empty(N, dtype=scale_dtype, device=W.device)
+    b = torch.empty(K, dtype=scale_dtype, device=W.device)
+    _check(lib.obl_svid(_ptr(W), dtype_code(W.dtype), N, K, iters, _ptr(packed), _ptr(a), _ptr(b),
+                        dtype_code(scale_dtype), _stream(W)), "obl_svid")
+    return packed, a, b

@@ -220,6 +220,39 @@ obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
   }
 }
 
+obl_status obl_svid(const void* W, obl_dtype w_dtype, int64_t N, int64_t K, int iters, uint32_t* packed,
+                    void* a, void* b, obl_dtype scale_dtype, void* stream) {
+  try {
+    if (!W || !packed || !a || !b) return OBL_ERR_NULL;
+    if (N < 1 || K < 1 || K % 32 != 0 || iters < 1 || iters > 100000) return OBL_ERR_SHAPE;
+    if (w_dtype != OBL_F32 && w_dtype != OBL_F16 && w_dtype != OBL_BF16) return OBL_ERR_DTYPE;
+    if (scale_dtype != OBL_F32 && scale_dtype != OBL_F16) return OBL_ERR_DTYPE;
+    const int ws = elem_size(w_dtype), ss = elem_size(scale_dtype);
+    int64_t wb = checked_bytes(N, K, ws), pb = checked_bytes(N, K / 32, 4);
+    int64_t ab = checked_bytes(N, 1, ss), bb = checked_bytes(K, 1, ss);
+    if (wb < 0 || pb < 0 || ab < 0 || bb < 0) return OBL_ERR_SHAPE;
+    if (!aligned(W, ws) || !aligned(packed, 4) || !aligned(a, ss) || !aligned(b, ss)) return OBL_ERR_ALIGN;
+    const Range rw = range_of(W, wb);
+    const Range outs[3] = {range_of(packed, pb), range_of(a, ab), range_of(b, bb)};
+    for (int o = 0; o < 3; ++o) {
+      if (overlap(outs[o], rw)) return OBL_ERR_ALIAS;
+      for (int p = o + 1; p < 3; ++p)
+        if (overlap(outs[o], outs[p])) return OBL_ERR_ALIAS;
+    }
+    DeviceInfo dev;
+    if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+    Scratch sc{};
+    if (scratch_reserve(dev.device, svid_workspace_floats(N, K), &sc) != hipSuccess) return OBL_ERR_HIP;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = launch_pack_signs(W, w_dtype, N, K, packed, hs);
+    if (e == hipSuccess) e = launch_svid(W, w_dtype, N, K, iters, a, b, scale_dtype, sc.partials, hs);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+    return OBL_OK;
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
 obl_status obl_transpose_signs(const uint32_t* packed, int64_t rows, int64_t K, uint32_t* packed_t,
                                void* stream) {
   try {

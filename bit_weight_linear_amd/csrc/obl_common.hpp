@@ -45,6 +45,11 @@ template <> struct Store<bf16_t> {
     p->bits = static_cast<uint16_t>(bf16_bits_rne(v));
   }
 };
+template <> struct Store<f16_t> {
+  static __device__ __forceinline__ void put(f16_t* p, float v) {   // round to nearest even
+    p->bits = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+  }
+};
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's 16 bytes land at lds_wave_base + 16*l, where lds_wave_base must be

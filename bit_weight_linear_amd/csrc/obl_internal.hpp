@@ -39,6 +39,9 @@ hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out);
 hipError_t launch_pack_signs(const void* S, int s_dtype, int64_t rows, int64_t K, uint32_t* P,
                              hipStream_t stream);
 hipError_t launch_gemv_lut(const LinearArgs& a, const DeviceInfo& dev);
+size_t svid_workspace_floats(int64_t N, int64_t K);
+hipError_t launch_svid(const void* W, int w_dtype, int64_t N, int64_t K, int iters, void* a, void* b,
+                       int scale_dtype, float* ws, hipStream_t st);
 hipError_t launch_transpose_signs(const uint32_t* P, int64_t rows, int64_t K, uint32_t* PT, hipStream_t st);
 hipError_t launch_backward_grads(int x_dtype, int scale_dtype, int dx_dtype, const void* dY, const void* X,
                                  const float* T, const float* U, const void* b, int64_t M, int64_t K,

@@ -23,7 +23,9 @@
  *    is enqueued, and buffers must stay alive until that work completes.
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer
  *    to caller memory after a call returns.  For its own split-K partial sums
- *    (decode sizes, M <= 16) it keeps one scratch buffer per device, allocated
+ *    (decode sizes, M <= 16), the bf16 copy of the DBF intermediate at
+ *    prefill sizes and the vectors of obl_svid it keeps one scratch buffer per
+ *    device, allocated
  *    with hipMalloc on the first call that needs it (at least 32 MiB), grown
  *    when a larger one is needed (after a device synchronise) and held until
  *    process exit.  Calls that overlap in time on one device (several streams
@@ -124,6 +126,24 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const uint32_t* S1_packed, int64_t N,
                       const void* b, const void* m, const void* a, obl_dtype scale_dtype,
                       float* workspace, void* Y, obl_dtype y_dtype, void* stream);
+
+/*
+ * obl_svid -- Sign-Value-Independent Decomposition of a dense weight:
+ *   W ≈ W_sign ⊙ (a b^T).  OneBit page, "rank-1 approximation" block and
+ *   proposition 2: W_sign = Sign(W) and a b^T is the rank-1 approximation of
+ *   |W|: σ1 u1 v1^T of its leading singular triple, split as a = sqrt(σ1) u1,
+ *   b = sqrt(σ1) v1 with the (nonnegative) singular vectors of |W|.
+ *   W       [N][K] dense, w_dtype OBL_F32, OBL_F16 or OBL_BF16, device.
+ *   iters   power-iteration steps (each reads |W| twice); >= 1.
+ *   packed  [N][K/32] Sign(W) (format above; 0 and -0 pack as +1), written.
+ *   a [N], b [K] scale_dtype (OBL_F32 or OBL_F16), written.
+ *   Uses the library's per-device scratch (see Ownership); sums are fp32 in a
+ *   fixed order.  Errors: OBL_ERR_NULL, OBL_ERR_SHAPE (N, K < 1, K % 32 != 0,
+ *   iters out of [1, 100000]), OBL_ERR_DTYPE, OBL_ERR_ALIGN, OBL_ERR_ALIAS,
+ *   OBL_ERR_HIP.
+ */
+obl_status obl_svid(const void* W, obl_dtype w_dtype, int64_t N, int64_t K, int iters, uint32_t* packed,
+                    void* a, void* b, obl_dtype scale_dtype, void* stream);
 
 /*
  * obl_transpose_signs -- packed signs of the transposed sign matrix.

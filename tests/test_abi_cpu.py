@@ -175,3 +175,18 @@ def bwd(dY=GY, X_=X, xd=b.OBL_BF16, M=4, K=4096, W_=W, Wt=WT, N=4096, a=A, bb=B_
 ])
 def test_backward_rejects(kw, code):
     assert bwd(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, b.OBL_F16, 64, 64, 8, W, A, B_), b.OBL_ERR_NULL),
+    ((X, b.OBL_F16, 64, 64, 8, None, A, B_), b.OBL_ERR_NULL),
+    ((X, b.OBL_F16, 64, 48, 8, W, A, B_), b.OBL_ERR_SHAPE),
+    ((X, b.OBL_F16, 0, 64, 8, W, A, B_), b.OBL_ERR_SHAPE),
+    ((X, b.OBL_F16, 64, 64, 0, W, A, B_), b.OBL_ERR_SHAPE),
+    ((X, b.OBL_I8, 64, 64, 8, W, A, B_), b.OBL_ERR_DTYPE),
+    ((P(0x10_0000_0001), b.OBL_F16, 64, 64, 8, W, A, B_), b.OBL_ERR_ALIGN),
+    ((X, b.OBL_F16, 64, 64, 8, P(0x10_0000_0000 + 64), A, B_), b.OBL_ERR_ALIAS),
+    ((X, b.OBL_F16, 64, 64, 8, W, A, A), b.OBL_ERR_ALIAS),
+])
+def test_svid_rejects(args, code):
+    assert L.obl_svid(*args, b.OBL_F16, None) == code
