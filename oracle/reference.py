@@ -53,6 +53,7 @@ __all__ = [
     "transpose_signs",
     "onebit_backward",
     "backward_error_scales",
+    "layernorm_rows",
 ]
 
 
@@ -247,6 +248,26 @@ def backward_error_scales(X, a, b, dY):
     s_da = np.abs(dY).T @ xb
     s_db = np.abs(X).T @ ga
     return s_dx, s_da, s_db
+
+
+# --------------------------------------------------------------------------
+# LayerNorm after the layer (OneBit page, "知识蒸馏" block: Z = LayerNorm(Y)).
+# The page gives neither epsilon nor affine parameters; the reading used is the
+# textbook per-row normalisation with a caller-given epsilon (1e-5 by default)
+# and optional elementwise gamma, beta.
+# --------------------------------------------------------------------------
+def layernorm_rows(Y, eps: float = 1e-5, gamma=None, beta=None) -> np.ndarray:
+    """``z_ij = (y_ij - mean_i) / sqrt(var_i + eps) * gamma_j + beta_j`` with the
+    row mean and the biased (population) row variance."""
+    Y = _f64(Y)
+    mu = Y.mean(axis=1, keepdims=True)
+    var = ((Y - mu) ** 2).mean(axis=1, keepdims=True)
+    Z = (Y - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        Z = Z * _f64(gamma)[None, :]
+    if beta is not None:
+        Z = Z + _f64(beta)[None, :]
+    return Z
 
 
 # --------------------------------------------------------------------------

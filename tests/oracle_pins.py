@@ -329,6 +329,47 @@ def pin_backward_bruteforce(onebit_backward, seed=37):
 BACKWARD_PINS = (pin_backward_finite_differences, pin_backward_bruteforce)
 
 
+def pin_layernorm_closed_forms(layernorm_rows):
+    """Constant rows normalise to beta; a row of +c / -c in equal numbers to
+    ±c / sqrt(c^2 + eps); the affine parameters act elementwise."""
+    errs = []
+    Y = np.full((2, 8), 3.5)
+    if not np.allclose(layernorm_rows(Y, 1e-5), 0.0, atol=0):
+        errs.append("constant row not mapped to 0")
+    c, eps = 2.0, 1e-3
+    Y = np.array([[c, -c] * 4])
+    ref = np.array([[1.0, -1.0] * 4]) * c / np.sqrt(c * c + eps)
+    if not np.allclose(layernorm_rows(Y, eps), ref, rtol=1e-14, atol=0):
+        errs.append("±c row")
+    g, bta = np.arange(1.0, 9.0), np.linspace(-1, 1, 8)
+    if not np.allclose(layernorm_rows(Y, eps, g, bta), ref * g + bta, rtol=1e-14, atol=1e-15):
+        errs.append("affine")
+    return errs
+
+
+def pin_layernorm_invariants_and_bruteforce(layernorm_rows, seed=47):
+    """Row mean 0 and mean square var / (var + eps), and pure-Python loops."""
+    rng = np.random.default_rng(seed)
+    Y = rng.standard_normal((3, 17)) * 5 + 2
+    eps = 0.25
+    Z = layernorm_rows(Y, eps)
+    errs = []
+    for i in range(3):
+        row = [float(v) for v in Y[i]]
+        mu = sum(row) / len(row)
+        var = sum((v - mu) ** 2 for v in row) / len(row)
+        for j, v in enumerate(row):
+            ref = (v - mu) / (var + eps) ** 0.5
+            if abs(Z[i, j] - ref) > 1e-13:
+                errs.append(f"brute force ({i},{j})")
+        if abs(Z[i].mean()) > 1e-13 or abs((Z[i] ** 2).mean() - var / (var + eps)) > 1e-12:
+            errs.append(f"invariants row {i}")
+    return errs
+
+
+LAYERNORM_PINS = (pin_layernorm_closed_forms, pin_layernorm_invariants_and_bruteforce)
+
+
 def run(pins, *fns):
     out = []
     for p in pins:

@@ -233,3 +233,32 @@ BACKWARD_MUTANTS = {
 @pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
 def test_backward_mutants_fail_some_pin(name):
     assert P.run(P.BACKWARD_PINS, BACKWARD_MUTANTS[name]) != [], f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------- LayerNorm after the layer
+@pytest.mark.parametrize("pin", P.LAYERNORM_PINS, ids=lambda p: p.__name__)
+def test_layernorm_pins(pin):
+    assert pin(O.layernorm_rows) == []
+
+
+def _ln_unbiased(Y, eps=1e-5, gamma=None, beta=None):
+    Y = np.asarray(Y, float)
+    mu = Y.mean(1, keepdims=True)
+    var = ((Y - mu) ** 2).sum(1, keepdims=True) / (Y.shape[1] - 1)
+    return (Y - mu) / np.sqrt(var + eps)
+
+
+LAYERNORM_MUTANTS = {
+    "unbiased_variance": _ln_unbiased,
+    "eps_outside_sqrt": lambda Y, eps=1e-5, gamma=None, beta=None: (
+        (np.asarray(Y, float) - np.asarray(Y, float).mean(1, keepdims=True))
+        / (np.asarray(Y, float).std(1, keepdims=True) + eps)),
+    "no_centering": lambda Y, eps=1e-5, gamma=None, beta=None: (
+        np.asarray(Y, float) / np.sqrt(np.asarray(Y, float).var(1, keepdims=True) + eps)),
+    "gamma_ignored": lambda Y, eps=1e-5, gamma=None, beta=None: O.layernorm_rows(Y, eps, None, beta),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYERNORM_MUTANTS))
+def test_layernorm_mutants_fail_some_pin(name):
+    assert P.run(P.LAYERNORM_PINS, LAYERNORM_MUTANTS[name]) != [], f"mutant {name} passed every pin"
