@@ -375,6 +375,55 @@ def main():
                                               "weight_read_GBps": round(passes * Wd.numel() * 2 / (ms8 * 1e-3) / 1e9, 1)}
         log(f"[bench] svid-11008x4096-f16-32iters: {ms8:.3f} ms per conversion")
         del Wd, P8, a8, b8
+        # LayerNorm after the layer: the row kernel alone at the prefill output shape
+        # (fp32 Y -> bf16 Z, fp16 gamma/beta), over 4 copies of Y so no replay hits in cache
+        M9, N9 = 2048, 14336
+        rng9 = np.random.default_rng(9)
+        Y9 = [torch.from_numpy(rng9.standard_normal((M9, N9)) * 2 + 1).to(torch.float32).cuda() for _ in range(4)]
+        g9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.5 + 1, "f16")).to(torch.float16).cuda()
+        be9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.1, "f16")).to(torch.float16).cuda()
+        Z9 = torch.empty((M9, N9), dtype=torch.bfloat16, device="cuda")
+        B.layernorm(Y9[0], 1e-5, g9, be9, out=Z9)
+        torch.cuda.synchronize()
+        r9 = np.array([0, 1, 777, M9 - 1])
+        y9h = Y9[0][torch.from_numpy(r9).cuda()].cpu().numpy().astype(np.float64)
+        z9ref = O.layernorm_rows(y9h, 1e-5, g9.float().cpu().numpy().astype(np.float64),
+                                 be9.float().cpu().numpy().astype(np.float64))
+        e9 = float(np.max(np.abs(Z9[torch.from_numpy(r9).cuda()].float().cpu().numpy() - z9ref)
+                          / (np.abs(z9ref) + 1.0)))
+        assert e9 <= 2.0 ** -7, "parity failed on the LayerNorm"
+        t9 = Timed(torch, [(lambda y=y: B.layernorm(y, 1e-5, g9, be9, out=Z9)) for y in Y9])
+        _, ms9 = t9.run(args.warmup, args.steps)
+        by9 = M9 * N9 * (4 + 2) + 2 * N9 * 2
+        sec["layernorm-2048x14336-f32-bf16"] = {
+            "us_per_launch": round(ms9 * 1e3, 3), "GBps": round(by9 / (ms9 * 1e-3) / 1e9, 1),
+            "hbm_frac": round(by9 / (ms9 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "algorithmic_bytes": by9, "parity_max_rel_error_sampled": float(f"{e9:.3e}")}
+        log(f"[bench] layernorm-2048x14336: {ms9 * 1e3:.2f} us, {by9 / (ms9 * 1e-3) / 1e9:.0f} GB/s")
+        del t9, Y9, Z9
+        # the decode layer followed by LayerNorm in one call (headline shape)
+        c10 = WL.workload(2)
+        X10 = torch.from_numpy(c10.X).to(torch.float32).to(torch.bfloat16).cuda()
+        W10 = B.pack_signs(torch.from_numpy(c10.W_sign).cuda())
+        a10 = torch.from_numpy(c10.a).to(torch.float32).to(torch.float16).cuda()
+        b10 = torch.from_numpy(c10.b).to(torch.float32).to(torch.float16).cuda()
+        reps10 = [(W10, a10, b10)] + [(W10.clone(), a10.clone(), b10.clone()) for _ in range(R - 1)]
+        ws10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
+        Z10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
+        B.linear_layernorm(X10, W10, a10, b10, 1e-5, workspace=ws10, out=Z10)
+        torch.cuda.synchronize()
+        y10 = O.onebit_linear(c10.X, c10.W_sign, c10.a, c10.b)
+        e10 = float(np.max(np.abs(Z10.cpu().numpy().astype(np.float64) - O.layernorm_rows(y10, 1e-5))))
+        assert e10 <= 1e-3, "parity failed on the layer + LayerNorm"
+        t10 = Timed(torch, [(lambda w=w, a=a, b=b: B.linear_layernorm(X10, w, a, b, 1e-5, workspace=ws10, out=Z10))
+                            for (w, a, b) in reps10])
+        _, ms10 = t10.run(args.warmup, args.steps)
+        sec[f"linear-layernorm-{c10.name}"] = {"us_per_call": round(ms10 * 1e3, 3),
+                                               "weight_GBps": round(wbytes / (ms10 * 1e-3) / 1e9, 1),
+                                               "max_abs_error_vs_oracle": float(f"{e10:.3e}"), "copies": R,
+                                               "launches_per_call": 2}
+        log(f"[bench] linear-layernorm-{c10.name}: {ms10 * 1e3:.2f} us per call")
+        del t10, reps10
         out["secondary"] = sec
 
     if args.copy_calibration_mib > 0:

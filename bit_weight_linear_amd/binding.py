@@ -23,12 +23,12 @@ lib = ctypes.CDLL(_LIB_PATH)
 
 # obl_status codes
 OBL_OK, OBL_ERR_NULL, OBL_ERR_SHAPE, OBL_ERR_DTYPE, OBL_ERR_ALIGN, OBL_ERR_ALIAS, OBL_ERR_HIP, \
-    OBL_ERR_INTERNAL = range(8)
+    OBL_ERR_INTERNAL, OBL_ERR_VALUE = range(9)
 # obl_dtype codes
 OBL_F32, OBL_F16, OBL_BF16, OBL_I8 = range(4)
 
 EXPORTS = ("obl_pack_signs", "obl_linear", "dbf_linear", "obl_transpose_signs", "obl_linear_backward",
-           "obl_svid", "obl_status_string", "obl_version")
+           "obl_svid", "obl_layernorm", "obl_linear_layernorm", "obl_status_string", "obl_version")
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 lib.obl_pack_signs.argtypes = [_vp, _int, _i64, _i64, _vp, _vp]
@@ -45,6 +45,12 @@ lib.obl_linear_backward.argtypes = [_vp, _vp, _int, _i64, _i64, _vp, _vp, _i64, 
 lib.obl_linear_backward.restype = _int
 lib.obl_svid.argtypes = [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _int, _vp]
 lib.obl_svid.restype = _int
+_f32 = ctypes.c_float
+lib.obl_layernorm.argtypes = [_vp, _int, _i64, _i64, _f32, _vp, _vp, _int, _vp, _int, _vp]
+lib.obl_layernorm.restype = _int
+lib.obl_linear_layernorm.argtypes = [_vp, _int, _i64, _i64, _vp, _i64, _vp, _vp, _int, _f32, _vp, _vp,
+                                     _vp, _vp, _int, _vp]
+lib.obl_linear_layernorm.restype = _int
 lib.obl_status_string.argtypes = [_int]
 lib.obl_status_string.restype = ctypes.c_char_p
 lib.obl_version.argtypes = []
@@ -174,3 +180,45 @@ def svid(W: torch.Tensor, iters: int = 32, scale_dtype: torch.dtype = torch.floa
     _check(lib.obl_svid(_ptr(W), dtype_code(W.dtype), N, K, iters, _ptr(packed), _ptr(a), _ptr(b),
                         dtype_code(scale_dtype), _stream(W)), "obl_svid")
     return packed, a, b
+
+
+def layernorm(Y: torch.Tensor, eps: float = 1e-5, gamma: Optional[torch.Tensor] = None,
+              beta: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Z = LayerNorm(Y) over rows (optional gamma, beta) through ``obl_layernorm``."""
+    _dev(Y, "Y")
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _dev(t, n)
+    M, N = Y.shape
+    affine = gamma if gamma is not None else beta
+    g_dtype = dtype_code(affine.dtype) if affine is not None else OBL_F32
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=Y.device)
+    _check(lib.obl_layernorm(_ptr(Y), dtype_code(Y.dtype), M, N, eps, _ptr(gamma), _ptr(beta), g_dtype,
+                             _ptr(out), dtype_code(out.dtype), _stream(Y)), "obl_layernorm")
+    return out
+
+
+def linear_layernorm(X: torch.Tensor, W_packed: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                     eps: float = 1e-5, gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None):
+    """Z = LayerNorm(((X ⊙ b) W_sign^T) ⊙ a) through ``obl_linear_layernorm``.
+
+    Returns (Z, workspace); the workspace holds the fp32 Y before normalisation."""
+    for t, n in ((X, "X"), (W_packed, "W_packed"), (a, "a"), (b, "b")):
+        _dev(t, n)
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _dev(t, n)
+    M, K = X.shape
+    N = W_packed.shape[0]
+    if workspace is None:
+        workspace = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    _check(lib.obl_linear_layernorm(_ptr(X), dtype_code(X.dtype), M, K, _ptr(W_packed), N, _ptr(a), _ptr(b),
+                                    dtype_code(a.dtype), eps, _ptr(gamma), _ptr(beta), _ptr(workspace),
+                                    _ptr(out), dtype_code(out.dtype), _stream(X)), "obl_linear_layernorm")
+    return out, workspace

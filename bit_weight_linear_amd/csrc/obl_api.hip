@@ -4,6 +4,7 @@
 // device state (and the error paths can be exercised without a GPU).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -103,6 +104,28 @@ bool linear_dtypes_ok(obl_dtype x, obl_dtype s, obl_dtype y) {
          (y == OBL_F32 || y == OBL_BF16);
 }
 
+// Checks shared by obl_layernorm and obl_linear_layernorm on the LayerNorm
+// operands: eps, the optional affine vectors and Z.  `ins` are the ranges Z
+// must not overlap.
+obl_status check_layernorm(int64_t M, int64_t N, float eps, const void* gamma, const void* beta,
+                           obl_dtype g_dtype, const void* Z, obl_dtype z_dtype, const Range* ins, int n_ins) {
+  if (M > 0 && !Z) return OBL_ERR_NULL;
+  if (!valid_dtype(z_dtype) || (z_dtype != OBL_F32 && z_dtype != OBL_BF16)) return OBL_ERR_DTYPE;
+  if ((gamma || beta) && g_dtype != OBL_F32 && g_dtype != OBL_F16) return OBL_ERR_DTYPE;
+  if (!std::isfinite(eps) || eps < 0.f) return OBL_ERR_VALUE;
+  const int gs = (gamma || beta) ? elem_size(g_dtype) : 1, zs = elem_size(z_dtype);
+  const int64_t gb = checked_bytes(N, 1, gs), zb = checked_bytes(M, N, zs);
+  if (gb < 0 || zb < 0 || M > 0x7fffffff) return OBL_ERR_SHAPE;
+  if ((gamma && !aligned(gamma, gs)) || (beta && !aligned(beta, gs)) || (M > 0 && !aligned(Z, zs)))
+    return OBL_ERR_ALIGN;
+  const Range rz = range_of(Z, zb);
+  if ((gamma && overlap(rz, range_of(gamma, gb))) || (beta && overlap(rz, range_of(beta, gb))))
+    return OBL_ERR_ALIAS;
+  for (int i = 0; i < n_ins; ++i)
+    if (overlap(rz, ins[i])) return OBL_ERR_ALIAS;
+  return OBL_OK;
+}
+
 }  // namespace
 
 hipError_t device_info(DeviceInfo* out) {
@@ -161,6 +184,7 @@ const char* obl_status_string(obl_status s) {
     case OBL_ERR_ALIAS: return "OBL_ERR_ALIAS: output overlaps another argument";
     case OBL_ERR_HIP: return "OBL_ERR_HIP: HIP runtime error";
     case OBL_ERR_INTERNAL: return "OBL_ERR_INTERNAL: internal error";
+    case OBL_ERR_VALUE: return "OBL_ERR_VALUE: scalar argument out of range";
   }
   return "OBL_ERR_UNKNOWN";
 }
@@ -325,6 +349,73 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
     if (st != OBL_OK) return st;
     hipError_t e = launch_backward_grads(x_dtype, scale_dtype, dx_dtype, dY, X, T, U, b, M, K, N, dX, da,
                                          db, hs);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+    return OBL_OK;
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
+obl_status obl_layernorm(const void* Y, obl_dtype y_dtype, int64_t M, int64_t N, float eps,
+                         const void* gamma, const void* beta, obl_dtype affine_dtype,
+                         void* Z, obl_dtype z_dtype, void* stream) {
+  try {
+    if (M < 0 || N < 1) return OBL_ERR_SHAPE;
+    if (M > 0 && !Y) return OBL_ERR_NULL;
+    if (!valid_dtype(y_dtype) || (y_dtype != OBL_F32 && y_dtype != OBL_BF16)) return OBL_ERR_DTYPE;
+    const int ys = elem_size(y_dtype);
+    const int64_t yb = checked_bytes(M, N, ys);
+    if (yb < 0) return OBL_ERR_SHAPE;
+    const Range ry = range_of(Y, yb);
+    obl_status st = check_layernorm(M, N, eps, gamma, beta, affine_dtype, Z, z_dtype, &ry, 1);
+    if (st != OBL_OK) return st;
+    if (M > 0 && !aligned(Y, ys)) return OBL_ERR_ALIGN;
+    if (M == 0) return OBL_OK;
+    hipError_t e = launch_layernorm_rows(Y, y_dtype, M, N, eps, gamma, beta, affine_dtype, Z, z_dtype,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
+    return OBL_OK;
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
+  }
+}
+
+obl_status obl_linear_layernorm(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                                const uint32_t* W_packed, int64_t N,
+                                const void* a, const void* b, obl_dtype scale_dtype,
+                                float eps, const void* gamma, const void* beta,
+                                float* workspace, void* Z, obl_dtype z_dtype, void* stream) {
+  try {
+    if (M < 0 || K < 1 || N < 1 || K % 32 != 0) return OBL_ERR_SHAPE;
+    if (!W_packed || !a || !b) return OBL_ERR_NULL;
+    if (M > 0 && (!X || !workspace)) return OBL_ERR_NULL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype)) return OBL_ERR_DTYPE;
+    if (!linear_dtypes_ok(x_dtype, scale_dtype, OBL_F32)) return OBL_ERR_DTYPE;
+    const int xs = elem_size(x_dtype), ss = elem_size(scale_dtype);
+    int64_t xb = checked_bytes(M, K, xs), wb = checked_bytes(N, K / 32, 4);
+    int64_t ab = checked_bytes(N, 1, ss), bb = checked_bytes(K, 1, ss);
+    int64_t yb = checked_bytes(M, N, 4);
+    if (xb < 0 || wb < 0 || ab < 0 || bb < 0 || yb < 0) return OBL_ERR_SHAPE;
+    if ((M > 0 && (!aligned(X, xs) || !aligned(workspace, 4))) || !aligned(W_packed, 4) || !aligned(a, ss) ||
+        !aligned(b, ss))
+      return OBL_ERR_ALIGN;
+    const int64_t gb = (gamma || beta) ? checked_bytes(N, 1, ss) : 0;
+    const Range ins[7] = {range_of(X, xb), range_of(W_packed, wb), range_of(a, ab), range_of(b, bb),
+                          range_of(workspace, yb), range_of(gamma, gamma ? gb : 0),
+                          range_of(beta, beta ? gb : 0)};
+    // The workspace (Y) must not overlap the linear's inputs or gamma / beta.
+    for (int i = 0; i < 7; ++i)
+      if (i != 4 && overlap(ins[4], ins[i])) return OBL_ERR_ALIAS;
+    obl_status st = check_layernorm(M, N, eps, gamma, beta, scale_dtype, Z, z_dtype, ins, 5);
+    if (st != OBL_OK) return st;
+    Path path = choose_path(M, &st);
+    if (st != OBL_OK) return st;
+    if (M == 0) return OBL_OK;
+    hipStream_t hs = (hipStream_t)stream;
+    LinearArgs la{X, x_dtype, M, K, W_packed, N, b, a, scale_dtype, workspace, OBL_F32, hs};
+    st = run_linear(la, path);
+    if (st != OBL_OK) return st;
+    hipError_t e = launch_layernorm_rows(workspace, OBL_F32, M, N, eps, gamma, beta, scale_dtype, Z, z_dtype, hs);
     if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
     return OBL_OK;
   } catch (...) {

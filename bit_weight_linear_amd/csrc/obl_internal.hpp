@@ -46,6 +46,8 @@ hipError_t launch_transpose_signs(const uint32_t* P, int64_t rows, int64_t K, ui
 hipError_t launch_backward_grads(int x_dtype, int scale_dtype, int dx_dtype, const void* dY, const void* X,
                                  const float* T, const float* U, const void* b, int64_t M, int64_t K,
                                  int64_t N, void* dX, float* da, float* db, hipStream_t st);
+hipError_t launch_layernorm_rows(const void* Y, int y_dtype, int64_t M, int64_t N, float eps, const void* gamma,
+                                 const void* beta, int g_dtype, void* Z, int z_dtype, hipStream_t st);
 hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
 // Main prefill kernel (bf16 activations); launch_gemm_mfma dispatches to it.

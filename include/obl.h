@@ -58,7 +58,8 @@ typedef enum {
   OBL_ERR_ALIGN = 4,    /* a pointer is not aligned to its element size (packed words: 4 bytes) */
   OBL_ERR_ALIAS = 5,    /* an output overlaps an input or another output */
   OBL_ERR_HIP = 6,      /* the HIP runtime reported an error */
-  OBL_ERR_INTERNAL = 7  /* unexpected internal failure */
+  OBL_ERR_INTERNAL = 7, /* unexpected internal failure */
+  OBL_ERR_VALUE = 8     /* a scalar argument is out of range (e.g. a negative epsilon) */
 } obl_status;
 
 typedef enum {
@@ -182,6 +183,49 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
                                const void* a, const void* b, obl_dtype scale_dtype,
                                void* dX, obl_dtype dx_dtype, float* da, float* db,
                                float* workspace, void* stream);
+
+/*
+ * obl_layernorm -- Z = LayerNorm(Y) over each row of Y [M][N].
+ *   OneBit page, knowledge-distillation block: the layer output is
+ *   layer-normalised (Z = LayerNorm(Y)) before the distillation losses.  The
+ *   page gives no epsilon or affine parameters; both are the caller's:
+ *     μ_i = mean_j y_ij,  σ²_i = mean_j (y_ij - μ_i)²  (biased, two passes),
+ *     z_ij = (y_ij - μ_i) / sqrt(σ²_i + eps) · gamma_j + beta_j.
+ *   Y       [M][N], y_dtype OBL_F32 or OBL_BF16.
+ *   eps     finite and >= 0 (eps = 0 turns a constant row into NaN, as the
+ *           formula does); otherwise OBL_ERR_VALUE.
+ *   gamma, beta  [N] of affine_dtype (OBL_F32 or OBL_F16); either may be NULL
+ *           (gamma = 1, beta = 0).  affine_dtype is ignored when both are NULL.
+ *   Z       [M][N], z_dtype OBL_F32 or OBL_BF16, written; must not overlap
+ *           any input.
+ *   Arithmetic: fp32 sums in a fixed order (bitwise reproducible); the error
+ *   is a few fp32 ulps of (|y| + |μ|) / σ before the output cast.
+ *   Errors: OBL_ERR_NULL, OBL_ERR_SHAPE (M < 0, N < 1), OBL_ERR_DTYPE,
+ *           OBL_ERR_VALUE, OBL_ERR_ALIGN, OBL_ERR_ALIAS, OBL_ERR_HIP.
+ */
+obl_status obl_layernorm(const void* Y, obl_dtype y_dtype, int64_t M, int64_t N, float eps,
+                         const void* gamma, const void* beta, obl_dtype affine_dtype,
+                         void* Z, obl_dtype z_dtype, void* stream);
+
+/*
+ * obl_linear_layernorm -- Z = LayerNorm(((X ⊙ b) · W_sign^T) ⊙ a): the layer of
+ *   obl_linear followed by obl_layernorm in one call (OneBit page,
+ *   knowledge-distillation block: Y = [(X ⊙ g) W_±1^T] ⊙ h, then
+ *   Z = LayerNorm(Y)).
+ *   X, W_packed, a, b, scale_dtype: as obl_linear.
+ *   eps, gamma, beta: as obl_layernorm, with gamma and beta of scale_dtype.
+ *   workspace  float32 [M][N], caller-owned: after completion it holds Y in
+ *              fp32.  Must not overlap any other argument.
+ *   Z          [M][N], z_dtype OBL_F32 or OBL_BF16, written.
+ *   Arithmetic: Y follows obl_linear's rules for the same M; LayerNorm as
+ *   obl_layernorm on the fp32 Y.
+ *   Errors: as obl_linear and obl_layernorm.
+ */
+obl_status obl_linear_layernorm(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                                const uint32_t* W_packed, int64_t N,
+                                const void* a, const void* b, obl_dtype scale_dtype,
+                                float eps, const void* gamma, const void* beta,
+                                float* workspace, void* Z, obl_dtype z_dtype, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* obl_status_string(obl_status status);

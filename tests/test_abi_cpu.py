@@ -37,8 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in range(8):
-        assert L.obl_status_string(code)
+    for code in range(9):
+        assert L.obl_status_string(code) != b"OBL_ERR_UNKNOWN"
     assert L.obl_status_string(99) == b"OBL_ERR_UNKNOWN"
     assert L.obl_version() >= 100
 
@@ -190,3 +190,73 @@ def test_backward_rejects(kw, code):
 ])
 def test_svid_rejects(args, code):
     assert L.obl_svid(*args, b.OBL_F16, None) == code
+
+
+# ------------------------------------------------------------------ LayerNorm
+G_, BT = P(0x80_0000_0000), P(0x90_0000_0000)
+
+
+def ln(Y=Y, yd=b.OBL_F32, M=4, N=4096, eps=1e-5, g=G_, be=BT, gd=b.OBL_F16, Z=WS, zd=b.OBL_BF16):
+    return L.obl_layernorm(Y, yd, M, N, eps, g, be, gd, Z, zd, None)
+
+
+def test_layernorm_m0_is_noop():
+    assert ln(M=0) == b.OBL_OK
+    assert ln(M=0, Y=None, Z=None) == b.OBL_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Y=None), b.OBL_ERR_NULL),
+    (dict(Z=None), b.OBL_ERR_NULL),
+    (dict(M=-1), b.OBL_ERR_SHAPE),
+    (dict(N=0), b.OBL_ERR_SHAPE),
+    (dict(M=1 << 40, N=1 << 30), b.OBL_ERR_SHAPE),
+    (dict(yd=b.OBL_F16), b.OBL_ERR_DTYPE),
+    (dict(zd=b.OBL_I8), b.OBL_ERR_DTYPE),
+    (dict(gd=b.OBL_BF16), b.OBL_ERR_DTYPE),
+    (dict(eps=-1.0), b.OBL_ERR_VALUE),
+    (dict(eps=float("nan")), b.OBL_ERR_VALUE),
+    (dict(eps=float("inf")), b.OBL_ERR_VALUE),
+    (dict(Y=P(0x50_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(Z=P(0x60_0000_0001)), b.OBL_ERR_ALIGN),
+    (dict(g=P(0x80_0000_0001)), b.OBL_ERR_ALIGN),
+    (dict(Z=P(0x50_0000_0000 + 64)), b.OBL_ERR_ALIAS),     # Z inside Y
+    (dict(g=P(0x60_0000_0000 + 64)), b.OBL_ERR_ALIAS),     # gamma inside Z
+    (dict(be=P(0x60_0000_0000 + 64)), b.OBL_ERR_ALIAS),    # beta inside Z
+])
+def test_layernorm_rejects(kw, code):
+    assert ln(**kw) == code
+
+
+def test_layernorm_affine_dtype_ignored_without_affine():
+    # No gamma/beta: the affine dtype is not checked; M = 0 keeps it a no-op.
+    assert ln(M=0, g=None, be=None, gd=b.OBL_BF16) == b.OBL_OK
+
+
+def lln(X=X, xd=b.OBL_BF16, M=2, K=4096, W=W, N=4096, a=A, bb=B_, sd=b.OBL_F16, eps=1e-5, g=G_, be=BT,
+        ws=S1, Z=WS, zd=b.OBL_F32):
+    return L.obl_linear_layernorm(X, xd, M, K, W, N, a, bb, sd, eps, g, be, ws, Z, zd, None)
+
+
+def test_linear_layernorm_m0_is_noop():
+    assert lln(M=0) == b.OBL_OK
+    assert lln(M=0, X=None, ws=None, Z=None) == b.OBL_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), b.OBL_ERR_NULL),
+    (dict(ws=None), b.OBL_ERR_NULL),
+    (dict(Z=None), b.OBL_ERR_NULL),
+    (dict(K=100), b.OBL_ERR_SHAPE),
+    (dict(xd=b.OBL_F16), b.OBL_ERR_DTYPE),
+    (dict(sd=b.OBL_BF16), b.OBL_ERR_DTYPE),
+    (dict(zd=b.OBL_F16), b.OBL_ERR_DTYPE),
+    (dict(eps=-0.5), b.OBL_ERR_VALUE),
+    (dict(ws=P(0x70_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(ws=P(0x10_0000_0000 + 256)), b.OBL_ERR_ALIAS),    # workspace inside X
+    (dict(ws=P(0x80_0000_0000 - 64)), b.OBL_ERR_ALIAS),     # workspace over gamma
+    (dict(Z=P(0x70_0000_0000 + 64)), b.OBL_ERR_ALIAS),      # Z inside workspace
+    (dict(Z=P(0x20_0000_0000 + 64)), b.OBL_ERR_ALIAS),      # Z inside W
+])
+def test_linear_layernorm_rejects(kw, code):
+    assert lln(**kw) == code
