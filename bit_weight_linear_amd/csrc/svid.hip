@@ -7,157 +7,386 @@
 // entrywise nonnegative, so power iteration from a positive start stays
 // positive and converges to them).
 //
-// Power iteration, every pass a bandwidth-bound read of the dense |W|:
-//   v̂ = 1/sqrt(K);  repeat: u = |W| v̂, û = u / ||u||;  v = |W|^T û, v̂ = v / ||v||
-//   finally u = |W| v̂, σ1 = ||u||, a = sqrt(σ1) u / σ1, b = sqrt(σ1) v̂.
-// Row pass: one wave per row, lanes over k, fixed-order wave reduction.
-// Column pass: blocks of 256 columns x 64 rows write partial column sums; a
-// second kernel adds the row chunks in order and applies the 1/||u|| scale.
-// Norms: one block, fixed order.  All sums are fp32 and reproducible.
+// Power iteration; every pass is a bandwidth-bound read of the dense |W|:
+//   v = 1;  repeat: u = |W| v / ||v||;  v = |W|^T u / ||u||
+//   finally u = |W| v / ||v||, σ1 = ||u||, a = u / sqrt(σ1), b = sqrt(σ1) v / ||v||.
+// Three kernels per iteration, none of them a single workgroup:
+//  * row pass: a workgroup takes 8 rows (2 per wave), stages v through LDS
+//    in tiles shared by its 4 waves (the staging overlaps the weight loads),
+//    reads W with 16-byte loads, and also
+//    forms ||v||^2 from the tiles it stages (the same fixed-order sum in every
+//    workgroup, so every u_i is divided by the same value); it writes u and
+//    the workgroup's Σ u_i^2 (rows in order);
+//  * column pass: 4 columns per thread (one 8- or 16-byte load per row),
+//    64 rows per workgroup, partial column sums part[chunk][k];
+//  * column reduction: 32 threads per 4 columns add the chunks (lane l takes
+//    chunks l, l + 32, ...; lanes added in order), ||u|| from the row pass's
+//    per-workgroup sums (fixed order), v = Σ part / ||u||.
+// Loads are issued unconditionally with indexes clamped inside the matrix and
+// masked out of the sums (no per-lane branch around a load, so a thread's loads
+// are in flight together).  All sums are fp32 in a fixed order: bitwise
+// reproducible.
 #include "obl_common.hpp"
 #include "obl_internal.hpp"
 
 namespace obl {
 namespace {
 
-constexpr int SV_COLS = 256;     // columns per column-pass block
-constexpr int SV_ROWS = 64;      // rows per column-pass block
+constexpr int SV_RPB = 8;        // rows per row-pass workgroup (2 per wave)
+constexpr int SV_CHUNK = 64;     // rows per column-pass workgroup
+constexpr int SV_CPT = 4;        // columns per column-pass thread
+constexpr int SV_CLANES = 32;    // chunk lanes per column quad in the reduction
+constexpr int SV_RCOLS = 4 * (256 / SV_CLANES);   // columns per reduction workgroup (32)
 
 template <typename T> __device__ __forceinline__ float absval(T v) { return fabsf(to_f32(v)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// V consecutive elements as one raw load (16 bytes for V = 16 / sizeof(T), 8
+// bytes for 16-bit types at V = 4, one element at V = 1), and their absolute
+// values as floats.  Loading and converting are separate so that the loads of
+// a thread can all be issued before any of them is waited for.
+template <int V, typename T> struct Raw;
+template <typename T> struct Raw<1, T> {
+  using type = T;
+  static __device__ __forceinline__ type load(const T* p) { return *p; }
+  static __device__ __forceinline__ void abs(const type& q, float o[1]) { o[0] = absval(q); }
+};
+template <> struct Raw<4, float> {
+  using type = float4;
+  static __device__ __forceinline__ type load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  static __device__ __forceinline__ void abs(const type& q, float o[4]) {
+    o[0] = fabsf(q.x); o[1] = fabsf(q.y); o[2] = fabsf(q.z); o[3] = fabsf(q.w);
+  }
+};
+template <typename T> struct Raw<4, T> {   // 16-bit types: 8 bytes
+  using type = uint2;
+  static __device__ __forceinline__ type load(const T* p) { return *reinterpret_cast<const uint2*>(p); }
+  static __device__ __forceinline__ void abs(const type& q, float o[4]) {
+    const T* h = reinterpret_cast<const T*>(&q);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+    for (int e = 0; e < 4; ++e) o[e] = absval(h[e]);
+  }
+};
+template <typename T> struct Raw<8, T> {   // 16-bit types: 16 bytes
+  using type = uint4;
+  static __device__ __forceinline__ type load(const T* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ void abs(const type& q, float o[8]) {
+    const T* h = reinterpret_cast<const T*>(&q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = absval(h[e]);
+  }
+};
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// u[i] = scale · Σ_k |W_ik| v[k], scale = 1 / *vnorm.
-template <typename WT>
-__global__ __launch_bounds__(256) void svid_rows_kernel(const WT* __restrict__ W, int64_t N, int64_t K,
-                                                        const float* __restrict__ v,
-                                                        const float* __restrict__ vnorm,
-                                                        float* __restrict__ u) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;                                  // whole wave
-  const WT* w = W + row * K;
-  float acc = 0.f;
-  for (int64_t k = lane; k < K; k += 64) acc += absval(w[k]) * v[k];
-  acc = wave_sum(acc);
-  if (lane == 0) u[row] = acc / *vnorm;
+// Fixed-order sum over the 64 lanes (quad xors, half-mirror, mirror, then the
+// four 16-lane rows in order); wave-uniform result.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
-// part[c][k] = Σ_{i in chunk c} |W_ik| u[i].
-template <typename WT>
-__global__ __launch_bounds__(SV_COLS) void svid_cols_kernel(const WT* __restrict__ W, int64_t N, int64_t K,
-                                                            const float* __restrict__ u,
-                                                            float* __restrict__ part) {
-  const int64_t k = (int64_t)blockIdx.x * SV_COLS + threadIdx.x;
-  const int64_t c = blockIdx.y;
-  const int64_t i0 = c * SV_ROWS, i1 = min(i0 + SV_ROWS, N);
-  if (k >= K) return;
-  float acc = 0.f;
-  for (int64_t i = i0; i < i1; ++i) acc += absval(W[i * K + k]) * u[i];
-  part[c * K + k] = acc;
-}
-
-// v[k] = (Σ_c part[c][k]) / *unorm, chunks added in order.
-__global__ __launch_bounds__(256) void svid_cols_reduce_kernel(const float* __restrict__ part, int64_t chunks,
-                                                               int64_t K, const float* __restrict__ unorm,
-                                                               float* __restrict__ v) {
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k >= K) return;
-  float acc = 0.f;
-  for (int64_t c = 0; c < chunks; ++c) acc += part[c * K + k];
-  v[k] = acc / *unorm;
-}
-
-// *out = sqrt(Σ x²), one block of 1024 threads, fixed order.
-__global__ __launch_bounds__(1024) void svid_norm_kernel(const float* __restrict__ x, int64_t n,
-                                                         float* __restrict__ out) {
-  __shared__ float s[16];
-  float acc = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += x[i] * x[i];
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = acc;
+// Sum over a 256-thread workgroup (waves in order); `red` is used once.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Σ over x[0..n) of x^2, or of x, by a 256-thread workgroup in a fixed order
+// (n >= 1).  Loads go out 8 at a time (clamped indexes, masked terms) rather
+// than one round trip per element.
+template <bool SQUARE>
+__device__ __forceinline__ float block_total(const float* __restrict__ x, int64_t n, float* red) {
+  float s = 0.f;
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += 8 * 256) {
+    float t[8];
+    bool ok[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t i = i0 + (int64_t)r * 256;
+      ok[r] = i < n;
+      t[r] = x[ok[r] ? i : 0];
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s += ok[r] ? (SQUARE ? t[r] * t[r] : t[r]) : 0.f;
+  }
+  return block_sum(s, red);
+}
+
+// ---------------------------------------------------------------- row pass
+// Barrier for LDS traffic only: wait for this wave's LDS operations, then
+// s_barrier.  __syncthreads() would also wait for every global load in flight
+// (its fence drains vmcnt), i.e. for the weight loads issued ahead of it.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// u[i] = Σ_k |W_ik| v[k] / ||v||;  upart[block] = Σ over its rows of u[i]^2.
+// Element (j, e) of lane l in a tile is column t0 + (64 j + l) · V + e.  Per
+// tile: the v loads for staging (L2), then the 16 weight loads (HBM), then v is
+// written to LDS once its loads land (memory returns in issue order, so this
+// waits only for v) and the weights stream in behind the barrier.
+template <typename WT, int V>
+__global__ __launch_bounds__(256) void svid_rows_kernel(const WT* __restrict__ W, int64_t N, int64_t K,
+                                                        const float* __restrict__ v, float* __restrict__ u,
+                                                        float* __restrict__ upart) {
+  constexpr int TILE = 512 * V;
+  constexpr int NVL = TILE >= 1024 ? TILE / 1024 : 1;    // float4 staging loads per thread
+  // At least NVL · 1024 floats: every staging store lands inside, also past
+  // the tile's end (those slots are never read).
+  __shared__ __align__(16) float vs[TILE < 1024 ? 1024 : TILE];
+  __shared__ float red[4];
+  __shared__ float uu[SV_RPB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * SV_RPB + 2 * wave;
+  const WT* w0 = W + min(r0, N - 1) * K;
+  const WT* w1 = W + min(r0 + 1, N - 1) * K;
+  float acc0 = 0.f, acc1 = 0.f, vsq = 0.f;
+  for (int64_t t0 = 0; t0 < K; t0 += TILE) {
+    const int tl = (int)min((int64_t)TILE, K - t0);      // a multiple of 32 (K % 32 == 0)
+    float4 vv[NVL];
+    bool okv[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int f = (256 * i + tid) * 4;
+      okv[i] = f < tl;
+      vv[i] = *reinterpret_cast<const float4*>(v + t0 + (okv[i] ? f : 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    typename Raw<V, WT>::type q0[8], q1[8];
+    bool ok[8];
+    int ec[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = (64 * j + lane) * V;
+      ok[j] = e < tl;
+      ec[j] = ok[j] ? e : tl - V;
+      q0[j] = Raw<V, WT>::load(w0 + t0 + ec[j]);
+      q1[j] = Raw<V, WT>::load(w1 + t0 + ec[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (t0 > 0) lds_barrier();                           // every wave is done reading the previous tile
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int f = (256 * i + tid) * 4;
+      reinterpret_cast<float4*>(vs)[f >> 2] = vv[i];     // unconditional: no branch for the load to sink into
+      vsq += okv[i] ? ((vv[i].x * vv[i].x + vv[i].y * vv[i].y) + (vv[i].z * vv[i].z + vv[i].w * vv[i].w)) : 0.f;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float a0[V], a1[V], x[V];
+      Raw<V, WT>::abs(q0[j], a0);
+      Raw<V, WT>::abs(q1[j], a1);
+      if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < V; e += 4) {
+          const float4 t = reinterpret_cast<const float4*>(vs)[(ec[j] + e) >> 2];
+          x[e] = t.x; x[e + 1] = t.y; x[e + 2] = t.z; x[e + 3] = t.w;
+        }
+      } else {
+        x[0] = vs[ec[j]];
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        acc0 += ok[j] ? a0[e] * x[e] : 0.f;
+        acc1 += ok[j] ? a1[e] * x[e] : 0.f;
+      }
+    }
+  }
+  const float vnorm = sqrtf(block_sum(vsq, red));
+  const float s0 = wave_sum(acc0) / vnorm, s1 = wave_sum(acc1) / vnorm;
+  if (lane == 0) {
+    if (r0 < N) u[r0] = s0;
+    if (r0 + 1 < N) u[r0 + 1] = s1;
+    uu[2 * wave] = r0 < N ? s0 * s0 : 0.f;
+    uu[2 * wave + 1] = r0 + 1 < N ? s1 * s1 : 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {
     float t = 0.f;
-    for (int w = 0; w < 16; ++w) t += s[w];
-    *out = sqrtf(t);
+#pragma unroll
+    for (int r = 0; r < SV_RPB; ++r) t += uu[r];
+    upart[blockIdx.x] = t;
   }
 }
 
-// x[k] /= *norm in place.
-__global__ __launch_bounds__(256) void svid_scale_kernel(float* x, int64_t n, const float* __restrict__ norm) {
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k < n) x[k] = x[k] / *norm;
+// ---------------------------------------------------------------- column pass
+// part[c][k..k+CV) = Σ_{i in chunk c} |W_ik| u[i].
+template <typename WT, int CV>
+__global__ __launch_bounds__(256) void svid_cols_kernel(const WT* __restrict__ W, int64_t N, int64_t K,
+                                                        const float* __restrict__ u, float* __restrict__ part) {
+  const int64_t k = ((int64_t)blockIdx.x * 256 + threadIdx.x) * CV;
+  const int64_t c = blockIdx.y;
+  const int64_t i0 = c * SV_CHUNK, i1 = min(i0 + SV_CHUNK, N);
+  if (k >= K) return;                                    // no barrier in this kernel
+  float acc[CV];
+#pragma unroll
+  for (int e = 0; e < CV; ++e) acc[e] = 0.f;
+  for (int64_t i = i0; i < i1; i += 8) {
+    typename Raw<CV, WT>::type q[8];
+    float ui[8];
+    bool ok[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ok[r] = i + r < i1;
+      const int64_t ri = ok[r] ? i + r : i1 - 1;
+      q[r] = Raw<CV, WT>::load(W + ri * K + k);
+      ui[r] = u[ri];
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float w[CV];
+      Raw<CV, WT>::abs(q[r], w);
+#pragma unroll
+      for (int e = 0; e < CV; ++e) acc[e] += ok[r] ? w[e] * ui[r] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < CV; ++e) part[c * K + k + e] = acc[e];
 }
 
-__global__ void svid_init_kernel(float* __restrict__ v, int64_t K, float* __restrict__ vnorm) {
+// ---------------------------------------------------------------- column reduction
+// v[k] = Σ_c part[c][k] / ||u||, ||u||^2 = Σ_b upart[b].  Workgroup = SV_RCOLS
+// columns: thread (l, q) sums chunks l, l + SV_CLANES, ... of columns
+// 4q..4q+3; the SV_CLANES lane sums are then added in lane order.
+__global__ __launch_bounds__(256) void svid_vreduce_kernel(const float* __restrict__ part, int64_t chunks,
+                                                           int64_t K, const float* __restrict__ upart,
+                                                           int64_t nub, float* __restrict__ v) {
+  __shared__ float ps[SV_CLANES][SV_RCOLS + 1];
+  __shared__ float red[4];
+  const int tid = threadIdx.x, q = tid % (SV_RCOLS / 4), l = tid / (SV_RCOLS / 4);
+  const int64_t k = (int64_t)blockIdx.x * SV_RCOLS + 4 * q;
+  const float unorm = sqrtf(block_total<false>(upart, nub, red));
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int64_t kc = k < K ? k : K - 4;                  // K % 4 == 0
+  for (int64_t c0 = l; c0 < chunks; c0 += 8 * SV_CLANES) {
+    float4 p[8];
+    bool ok[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t cr = c0 + (int64_t)r * SV_CLANES;
+      ok[r] = cr < chunks;
+      p[r] = *reinterpret_cast<const float4*>(part + (ok[r] ? cr : 0) * K + kc);   // chunk 0 always exists
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      acc[0] += ok[r] ? p[r].x : 0.f;
+      acc[1] += ok[r] ? p[r].y : 0.f;
+      acc[2] += ok[r] ? p[r].z : 0.f;
+      acc[3] += ok[r] ? p[r].w : 0.f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ps[l][4 * q + e] = acc[e];
+  __syncthreads();
+  if (tid < SV_RCOLS) {
+    const int64_t col = (int64_t)blockIdx.x * SV_RCOLS + tid;
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < SV_CLANES; ++r) s += ps[r][tid];
+    if (col < K) v[col] = s / unorm;
+  }
+}
+
+__global__ __launch_bounds__(256) void svid_init_kernel(float* __restrict__ v, int64_t K) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (k < K) v[k] = 1.f;
-  if (k == 0) *vnorm = sqrtf((float)K);
 }
 
-// a = sqrt(σ) u / σ (σ = *unorm), b = sqrt(σ) v (v already unit length).
+// a = u / sqrt(σ), b = sqrt(σ) v / ||v||, σ^2 = Σ upart (u is |W| v / ||v||).
 template <typename ST>
 __global__ __launch_bounds__(256) void svid_final_kernel(const float* __restrict__ u, int64_t N,
                                                          const float* __restrict__ v, int64_t K,
-                                                         const float* __restrict__ unorm,
+                                                         const float* __restrict__ upart, int64_t nub,
                                                          ST* __restrict__ a, ST* __restrict__ b) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const float sigma = *unorm;
+  __shared__ float red[2][4];
+  const float sigma = sqrtf(block_total<false>(upart, nub, red[0]));
+  const float vnorm = sqrtf(block_total<true>(v, K, red[1]));
   const float root = sqrtf(sigma);
-  if (i < N) Store<ST>::put(&a[i], root * (u[i] / sigma));
-  if (i < K) Store<ST>::put(&b[i], root * v[i]);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < N) Store<ST>::put(&a[i], u[i] / root);
+  if (i < K) Store<ST>::put(&b[i], root * (v[i] / vnorm));
+}
+
+struct Layout {
+  int64_t chunks, nub;
+  float *part, *v, *u, *upart;
+};
+
+// Workspace: part [chunks][K] first (16-byte aligned rows, K % 4 == 0), then
+// v [K], u [N], upart [nub].
+Layout layout(float* ws, int64_t N, int64_t K) {
+  Layout L;
+  L.chunks = (N + SV_CHUNK - 1) / SV_CHUNK;
+  L.nub = (N + SV_RPB - 1) / SV_RPB;
+  L.part = ws;
+  L.v = L.part + L.chunks * K;
+  L.u = L.v + K;
+  L.upart = L.u + N;
+  return L;
+}
+
+template <typename WT, typename ST, int V, int CV>
+hipError_t run(const WT* W, int64_t N, int64_t K, int iters, void* av, void* bv, float* ws, hipStream_t st) {
+  const Layout L = layout(ws, N, K);
+  const dim3 gr((unsigned)L.nub);
+  const dim3 gc((unsigned)((K / CV + 255) / 256), (unsigned)L.chunks);
+  const dim3 gv((unsigned)((K + SV_RCOLS - 1) / SV_RCOLS));
+  hipLaunchKernelGGL(svid_init_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, L.v, K);
+  for (int it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL((svid_rows_kernel<WT, V>), gr, dim3(256), 0, st, W, N, K, L.v, L.u, L.upart);
+    hipLaunchKernelGGL((svid_cols_kernel<WT, CV>), gc, dim3(256), 0, st, W, N, K, L.u, L.part);
+    hipLaunchKernelGGL(svid_vreduce_kernel, gv, dim3(256), 0, st, L.part, L.chunks, K, L.upart, L.nub, L.v);
+  }
+  hipLaunchKernelGGL((svid_rows_kernel<WT, V>), gr, dim3(256), 0, st, W, N, K, L.v, L.u, L.upart);
+  const int64_t nmax = N > K ? N : K;
+  hipLaunchKernelGGL((svid_final_kernel<ST>), dim3((unsigned)((nmax + 255) / 256)), dim3(256), 0, st, L.u, N,
+                     L.v, K, L.upart, L.nub, static_cast<ST*>(av), static_cast<ST*>(bv));
+  return hipGetLastError();
 }
 
 template <typename WT, typename ST>
-hipError_t run(const void* Wv, int64_t N, int64_t K, int iters, void* av, void* bv, float* ws, hipStream_t st) {
+hipError_t run_v(const void* Wv, int64_t N, int64_t K, int iters, void* a, void* b, float* ws, hipStream_t st) {
   const WT* W = static_cast<const WT*>(Wv);
-  const int64_t chunks = (N + SV_ROWS - 1) / SV_ROWS;
-  float* u = ws;                     // [N]
-  float* v = u + N;                  // [K]
-  float* part = v + K;               // [chunks][K]
-  float* scal = part + chunks * K;   // [0] = ||v||, [1] = ||u||
-  const dim3 gr((unsigned)((N + 3) / 4)), gc((unsigned)((K + SV_COLS - 1) / SV_COLS), (unsigned)chunks);
-  const dim3 gk((unsigned)((K + 255) / 256));
-  hipLaunchKernelGGL(svid_init_kernel, gk, dim3(256), 0, st, v, K, scal);
-  for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL((svid_rows_kernel<WT>), gr, dim3(256), 0, st, W, N, K, v, scal, u);
-    hipLaunchKernelGGL(svid_norm_kernel, dim3(1), dim3(1024), 0, st, u, N, scal + 1);
-    hipLaunchKernelGGL((svid_cols_kernel<WT>), gc, dim3(SV_COLS), 0, st, W, N, K, u, part);
-    hipLaunchKernelGGL(svid_cols_reduce_kernel, gk, dim3(256), 0, st, part, chunks, K, scal + 1, v);
-    hipLaunchKernelGGL(svid_norm_kernel, dim3(1), dim3(1024), 0, st, v, K, scal);
-  }
-  // v̂ = v / ||v||: fold into the last row pass (u = |W| v̂) and the final scale.
-  hipLaunchKernelGGL((svid_rows_kernel<WT>), gr, dim3(256), 0, st, W, N, K, v, scal, u);
-  hipLaunchKernelGGL(svid_norm_kernel, dim3(1), dim3(1024), 0, st, u, N, scal + 1);
-  // b needs v̂.
-  hipLaunchKernelGGL(svid_scale_kernel, gk, dim3(256), 0, st, v, K, scal);
-  const int64_t nmax = N > K ? N : K;
-  hipLaunchKernelGGL((svid_final_kernel<ST>), dim3((unsigned)((nmax + 255) / 256)), dim3(256), 0, st, u, N, v,
-                     K, scal + 1, static_cast<ST*>(av), static_cast<ST*>(bv));
-  return hipGetLastError();
+  // Vector loads need a 16-byte aligned base (rows are K · sizeof(WT) bytes,
+  // a multiple of 64 since K % 32 == 0).
+  constexpr int V = 16 / sizeof(WT);
+  if (reinterpret_cast<uintptr_t>(Wv) % 16 == 0) return run<WT, ST, V, SV_CPT>(W, N, K, iters, a, b, ws, st);
+  return run<WT, ST, 1, 1>(W, N, K, iters, a, b, ws, st);
 }
 
 template <typename WT>
 hipError_t run_s(int scale_dtype, const void* W, int64_t N, int64_t K, int iters, void* a, void* b, float* ws,
                  hipStream_t st) {
-  return scale_dtype == DT_F32 ? run<WT, float>(W, N, K, iters, a, b, ws, st)
-                               : run<WT, f16_t>(W, N, K, iters, a, b, ws, st);
+  return scale_dtype == DT_F32 ? run_v<WT, float>(W, N, K, iters, a, b, ws, st)
+                               : run_v<WT, f16_t>(W, N, K, iters, a, b, ws, st);
 }
 
 }  // namespace
 
 size_t svid_workspace_floats(int64_t N, int64_t K) {
-  const int64_t chunks = (N + SV_ROWS - 1) / SV_ROWS;
-  return (size_t)(N + K + chunks * K + 8);
+  const int64_t chunks = (N + SV_CHUNK - 1) / SV_CHUNK, nub = (N + SV_RPB - 1) / SV_RPB;
+  return (size_t)(chunks * K + K + N + nub + 64);
 }
 
 hipError_t launch_svid(const void* W, int w_dtype, int64_t N, int64_t K, int iters, void* a, void* b,
                        int scale_dtype, float* ws, hipStream_t st) {
+  if ((N + SV_RPB - 1) / SV_RPB > 0x7fffffff || (N + SV_CHUNK - 1) / SV_CHUNK > 65535) return hipErrorInvalidValue;
   if (w_dtype == DT_F32) return run_s<float>(scale_dtype, W, N, K, iters, a, b, ws, st);
   if (w_dtype == DT_F16) return run_s<f16_t>(scale_dtype, W, N, K, iters, a, b, ws, st);
   return run_s<bf16_t>(scale_dtype, W, N, K, iters, a, b, ws, st);

@@ -16,7 +16,7 @@ def _rel(x, ref):
     return float(np.max(np.abs(np.asarray(x, float) - ref)) / np.max(np.abs(ref)))
 
 
-@pytest.mark.parametrize("N,K", [(256, 512), (100, 96), (11008, 4096)])
+@pytest.mark.parametrize("N,K", [(256, 512), (100, 96), (300, 4128), (11008, 4096)])
 @pytest.mark.parametrize("w_dtype,s_dtype", [("f16", "f16"), ("bf16", "f32"), ("f32", "f32")])
 def test_svid_matches_oracle(N, K, w_dtype, s_dtype):
     G.say(f"svid N={N} K={K} W {w_dtype} scales {s_dtype}")
@@ -31,6 +31,31 @@ def test_svid_matches_oracle(N, K, w_dtype, s_dtype):
     ea, eb = _rel(G.host64(a), a_ref), _rel(G.host64(b), b_ref)
     G.say(f"  a {ea:.2e} b {eb:.2e}")
     assert ea <= tol and eb <= tol
+
+
+def test_svid_unaligned_weight_takes_scalar_path():
+    """W one element past a 16-byte boundary: the kernels fall back to scalar
+    loads and must give the same packing and scales within the tolerance."""
+    rng = np.random.default_rng(21)
+    N, K = 200, 1024
+    Wd = WL.round_to(rng.standard_normal((N, K)) * 0.02, "f16")
+    buf = torch.zeros(N * K + 1, dtype=torch.float16, device="cuda")
+    buf[1:] = G.dev(Wd, "f16").flatten()
+    P, a, b = B.svid(buf[1:].view(N, K), iters=32, scale_dtype=torch.float32)
+    torch.cuda.synchronize()
+    S_ref, a_ref, b_ref = O.svid(Wd)
+    assert np.array_equal(G.packed_host(P), O.pack_signs(S_ref))
+    assert _rel(G.host64(a), a_ref) <= 2e-5 and _rel(G.host64(b), b_ref) <= 2e-5
+
+
+def test_svid_reproducible():
+    rng = np.random.default_rng(22)
+    Wd = G.dev(WL.round_to(rng.standard_normal((1000, 2048)) * 0.02, "bf16"), "bf16")
+    r1 = B.svid(Wd, iters=8, scale_dtype=torch.float32)
+    r2 = B.svid(Wd, iters=8, scale_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
 
 
 def test_svid_recovers_planted_rank1_magnitudes():
