@@ -44,6 +44,17 @@
 //  * Epilogue: acc·a in fp32 (a staged in LDS), one cast to the output dtype.
 //    A lane holds four consecutive output columns per register quad, written
 //    as one 16-byte (fp32) or 8-byte (bf16) store.
+//  * Small grids (at most half as many tiles as CUs, e.g. M = 512 with
+//    N = 3072 is 28 tiles) split K: tiles x slices fill the CUs once, each
+//    slice writes fp32 partial sums and a second kernel adds the slices in
+//    order (fixed order: reproducible; accumulation stays fp32).  Measured
+//    on 512 x 4096 x 3072: 8 slices of 4 stages, 224 workgroups, ~31 us for
+//    the split kernel and ~11 us for the reduction, against ~99 us unsplit
+//    on 28 workgroups.  The split kernel's fixed cost is the burst of
+//    partial sums written when every workgroup ends together (51 MB here)
+//    and the reduction reading them back; counting that traffic, more
+//    slices of fewer stages stop paying at about 8.
+#include <algorithm>
 #include <type_traits>
 
 #include "obl_common.hpp"
@@ -101,11 +112,16 @@ constexpr int GW_XDMA = GW_BM * (GW_KT / 8) / 64 / 4;    // activation DMAs per 
 constexpr int GW_WCOLS = 512;                             // sign columns staged (>= GW_BN, 2 DMAs per wave)
 constexpr int GW_WDMA = GW_WCOLS / 64 / 4;                // sign DMAs per wave per stage (2)
 
-template <typename ST, typename YT, bool PRE>
+// SPLIT: block b takes tile b / nsplit and the 128-k stages
+// [s·per, min((s + 1)·per, K/128)) of slice s = b % nsplit, and writes its raw
+// fp32 sums (no output scale) to part[s][M][N]; gemm_split_reduce_kernel adds
+// the slices in order.
+template <typename ST, typename YT, bool PRE, bool SPLIT>
 __global__ __launch_bounds__(GW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W,
                       int64_t N, const ST* __restrict__ pre, const ST* __restrict__ post,
-                      YT* __restrict__ Y, bf16_t* __restrict__ Y2, int mt, int nt, int xcd_groups) {
+                      YT* __restrict__ Y, bf16_t* __restrict__ Y2, int mt, int nt, int xcd_groups,
+                      int nsplit, int per, float* __restrict__ part) {
   // Three stage buffers as distinct LDS objects: the K loop is unrolled by
   // three so every access names its buffer, and the compiler can tell a DMA
   // into one buffer from reads of another.
@@ -126,8 +142,11 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   const int l32 = lane & 31;
 
   const int64_t kw = K >> 5;
-  const int nk = (int)(K / GW_KT);
+  const int nk_all = (int)(K / GW_KT);
   const int tiles = mt * nt;
+  const int slice = SPLIT ? (int)(blockIdx.x % (unsigned)nsplit) : 0;
+  const int t0 = SPLIT ? slice * per : 0;                  // first stage of this block
+  const int nk = SPLIT ? min(per, nk_all - t0) : nk_all;   // stages of this block (>= 1)
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(N * kw * 4));
 
@@ -163,8 +182,8 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   const int wcol = wn * GW_WN + l32;       // + 32 c
 
   // XCD x (= blockIdx % 8) takes tiles [x·T/8, (x+1)·T/8), column index fastest.
-  int lin = blockIdx.x;
-  if (xcd_groups > 1) {
+  int lin = SPLIT ? (int)(blockIdx.x / (unsigned)nsplit) : (int)blockIdx.x;
+  if (!SPLIT && xcd_groups > 1) {
     const int per = tiles / xcd_groups;
     lin = (blockIdx.x % xcd_groups) * per + blockIdx.x / xcd_groups;
   }
@@ -191,9 +210,10 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   }
   auto dma = [&](u32x4 (*xs)[GW_KT / 8], u32x4* ws, int t) {
 #pragma unroll
-    for (int i = 0; i < GW_XDMA; ++i) dma16(xr, &xs[4 * (GW_XDMA * wave + i)][0], xo[i], (uint32_t)t * (GW_KT * 2));
+    for (int i = 0; i < GW_XDMA; ++i)
+      dma16(xr, &xs[4 * (GW_XDMA * wave + i)][0], xo[i], (uint32_t)(t0 + t) * (GW_KT * 2));
 #pragma unroll
-    for (int j = 0; j < GW_WDMA; ++j) dma16(wr, &ws[64 * (GW_WDMA * wave + j)], wo[j], (uint32_t)t * 16);
+    for (int j = 0; j < GW_WDMA; ++j) dma16(wr, &ws[64 * (GW_WDMA * wave + j)], wo[j], (uint32_t)(t0 + t) * 16);
   };
 
   dma(xa, wa, 0);
@@ -220,7 +240,7 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
     for (int c = 0; c < GW_FN; ++c) wv[c] = ws[wcol + 32 * c];
     u32x4 xf[2][GW_FM], mg[2];
     auto read_step = [&](int s, int b) {
-      mg[b] = PRE ? bt4[(t * GW_KT + 16 * s + 8 * g) >> 3] : ones;
+      mg[b] = PRE ? bt4[((t0 + t) * GW_KT + 16 * s + 8 * g) >> 3] : ones;
 #pragma unroll
       for (int i = 0; i < GW_FM; ++i) xf[b][i] = xs[xrow + 32 * i][(2 * s + g) ^ (lane & 15)];
     };
@@ -270,6 +290,30 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   // Epilogue.  acc[c][i][4q + e] = D[row n = 8q + 4g + e][col m = l32] of the
   // (c, i) fragment, i.e. Y[m0 + 32i + l32][n0 + 32c + 8q + 4g + e].
   const int64_t m0 = bm0 + wm * GW_WM;
+  if constexpr (SPLIT) {
+    float* pp = part + (int64_t)slice * M * N;
+#pragma unroll
+    for (int i = 0; i < GW_FM; ++i) {
+      const int64_t m = m0 + 32 * i + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int c = 0; c < GW_FN; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = bn0 + wn * GW_WN + 32 * c + 8 * q + 4 * g;
+          float* yp = pp + m * N + n;
+          const float v[4] = {acc[c][i][4 * q], acc[c][i][4 * q + 1], acc[c][i][4 * q + 2], acc[c][i][4 * q + 3]};
+          if (n + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) yp[e] = v[e];
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < GW_FM; ++i) {
     const int64_t m = m0 + 32 * i + l32;
@@ -313,19 +357,91 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   }
 }
 
+// Y[m][n] = (Σ_s part[s][m][n]) · post[n] with the slices added in order,
+// plus the optional bf16 copy Y2.  Four consecutive outputs per thread when
+// N % 4 == 0, else one.
+template <typename ST, typename YT, int V>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                                int64_t MN, int64_t N, const ST* __restrict__ post,
+                                                                YT* __restrict__ Y, bf16_t* __restrict__ Y2) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+  if (e0 >= MN) return;
+  const int64_t n0 = e0 % N;
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float p[8][V];
+    bool ok[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ok[r] = s0 + r < nsplit;
+      const float* src = part + (int64_t)(ok[r] ? s0 + r : 0) * MN + e0;
+      if constexpr (V == 4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(src);
+        p[r][0] = t.x; p[r][1] = t.y; p[r][2] = t.z; p[r][3] = t.w;
+      } else {
+        p[r][0] = src[0];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += ok[r] ? p[r][e] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const float y = acc[e] * (post ? to_f32(post[n0 + e]) : 1.f);
+    Store<YT>::put(&Y[e0 + e], y);
+    if (Y2) Store<bf16_t>::put(&Y2[e0 + e], y);
+  }
+}
+
+// Split count: small grids (fewer tiles than CUs; the kernel runs one
+// workgroup per CU) split K so that tiles · nsplit fills the CUs once, with at
+// least 4 stages per slice so the three-buffer pipeline still overlaps.
+int split_count(int64_t tiles, int64_t nk, int num_cus) {
+  if (tiles * 2 > num_cus) return 1;
+  int64_t s = num_cus / tiles;
+  s = std::min<int64_t>(s, nk / 4);
+  s = std::min<int64_t>(s, 16);
+  return (int)std::max<int64_t>(s, 1);
+}
+
 template <typename ST, typename YT, bool PRE>
 hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
   const int64_t mt = (a.M + GW_BM - 1) / GW_BM;
   const int64_t nt = (a.N + GW_BN - 1) / GW_BN;
   const int64_t tiles = mt * nt;
-  (void)dev;
-  const int64_t grid = tiles;
-  const int xcd = (tiles % 8 == 0) ? 8 : 1;
+  const int64_t nk = a.K / GW_KT;
   const size_t lds = (PRE ? a.K / 2 : 0) * sizeof(uint32_t);
-  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE>), dim3((unsigned)grid), dim3(GW_THREADS), lds,
+  int nsplit = split_count(tiles, nk, dev.num_cus);
+  if (nsplit > 1) {
+    const int per = (int)((nk + nsplit - 1) / nsplit);
+    nsplit = (int)((nk + per - 1) / per);                   // every slice non-empty
+    float* part = nullptr;
+    hipError_t e = split_reserve(dev.device, (size_t)nsplit * (size_t)(a.M * a.N), &part);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_wide_kernel<ST, float, PRE, true>), dim3((unsigned)(tiles * nsplit)),
+                       dim3(GW_THREADS), lds, a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
+                       static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post), nullptr, nullptr, (int)mt,
+                       (int)nt, 1, nsplit, per, part);
+    const int64_t MN = a.M * a.N;
+    if (a.N % 4 == 0)
+      hipLaunchKernelGGL((gemm_split_reduce_kernel<ST, YT, 4>), dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256),
+                         0, a.stream, part, nsplit, MN, a.N, static_cast<const ST*>(a.post), static_cast<YT*>(a.Y),
+                         static_cast<bf16_t*>(a.Y2));
+    else
+      hipLaunchKernelGGL((gemm_split_reduce_kernel<ST, YT, 1>), dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
+                         a.stream, part, nsplit, MN, a.N, static_cast<const ST*>(a.post), static_cast<YT*>(a.Y),
+                         static_cast<bf16_t*>(a.Y2));
+    return hipGetLastError();
+  }
+  const int xcd = (tiles % 8 == 0) ? 8 : 1;
+  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE, false>), dim3((unsigned)tiles), dim3(GW_THREADS), lds,
                      a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                      static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post),
-                     static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.Y2), (int)mt, (int)nt, xcd);
+                     static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.Y2), (int)mt, (int)nt, xcd, 1, 0, nullptr);
   return hipGetLastError();
 }
 

@@ -144,17 +144,15 @@ hipError_t device_info(DeviceInfo* out) {
   return hipSuccess;
 }
 
-hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  Scratch& s = g_scratch[device];
-  if (s.partial_floats >= partial_floats) {
-    *out = s;
-    return hipSuccess;
-  }
-  size_t pf = partial_floats;
-  if (pf < (size_t(8) << 20)) pf = size_t(8) << 20;  // at least 32 MiB of partial sums
+namespace {
+// Grow-only per-device buffer: at least 32 MiB; a larger request waits for the
+// device (work already enqueued may still use the old buffer), frees it and
+// allocates anew.  Caller holds g_mu.
+hipError_t grow(Scratch& s, size_t floats) {
+  if (s.partial_floats >= floats) return hipSuccess;
+  size_t pf = floats;
+  if (pf < (size_t(8) << 20)) pf = size_t(8) << 20;
   if (s.partials) {
-    // Work already enqueued may still use the old buffer.
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return e;
     (void)hipFree(s.partials);
@@ -164,6 +162,25 @@ hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out) {
   hipError_t e = hipMalloc(&p, pf * sizeof(float));
   if (e != hipSuccess) return e;
   s = Scratch{p, pf};
+  return hipSuccess;
+}
+std::unordered_map<int, Scratch> g_split;
+}  // namespace
+
+hipError_t split_reserve(int device, size_t floats, float** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Scratch& s = g_split[device];
+  hipError_t e = grow(s, floats);
+  if (e != hipSuccess) return e;
+  *out = s.partials;
+  return hipSuccess;
+}
+
+hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Scratch& s = g_scratch[device];
+  hipError_t e = grow(s, partial_floats);
+  if (e != hipSuccess) return e;
   *out = s;
   return hipSuccess;
 }

@@ -35,6 +35,9 @@ struct Scratch {
 
 hipError_t device_info(DeviceInfo* out);
 hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out);
+// A second per-device buffer for the prefill GEMM's split-K partial sums (used
+// while the first one may hold a DBF intermediate).  Same growth policy.
+hipError_t split_reserve(int device, size_t floats, float** out);
 
 hipError_t launch_pack_signs(const void* S, int s_dtype, int64_t rows, int64_t K, uint32_t* P,
                              hipStream_t stream);

@@ -85,9 +85,14 @@ def test_decode_path(M, K, N, dts):
     G.check_onebit(c, G.run_onebit(c, "decode"), "decode")
 
 
+# Small grids split K (bf16 x, K % 128 == 0): (256, 4096, 224) and (600, 4096, 449)
+# into 8 slices, (300, 1152, 672) into 2, (40, 2048, 98) into 4 with N % 4 != 0
+# (scalar partials and reduction), (200, 4736, 1000) into 8 uneven slices (37
+# stages of 128 k); (255, 512, 448) has too few stages to split.
 GEMM_CASES = [
     (17, 32, 16), (64, 96, 225), (255, 512, 448), (256, 4096, 224), (257, 160, 1000),
-    (600, 4096, 449), (33, 64, 33), (513, 384, 230), (300, 1152, 672),
+    (600, 4096, 449), (33, 64, 33), (513, 384, 230), (300, 1152, 672), (40, 2048, 98),
+    (200, 4736, 1000),
 ]
 GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("bf16", "f32", "bf16"),
                ("f32", "f32", "f32"), ("f32", "f16", "bf16")]
