@@ -22,15 +22,16 @@
  *    stream).  Every call is asynchronous on `stream`: it returns once the work
  *    is enqueued, and buffers must stay alive until that work completes.
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer
- *    to caller memory after a call returns.  For its own split-K partial sums
- *    (decode sizes, M <= 16), the bf16 copy of the DBF intermediate at
- *    prefill sizes and the vectors of obl_svid it keeps one scratch buffer per
- *    device, allocated
- *    with hipMalloc on the first call that needs it (at least 32 MiB), grown
- *    when a larger one is needed (after a device synchronise) and held until
- *    process exit.  Calls that overlap in time on one device (several streams
- *    or host threads) must not both use it -- serialise them -- and the first
- *    such call must not be made inside HIP stream capture.
+ *    to caller memory after a call returns.  It keeps two scratch buffers per
+ *    device: one for the decode kernels' split-K partial sums (M <= 16), the
+ *    bf16 copy of the DBF intermediate at prefill sizes and the vectors of
+ *    obl_svid, one for the prefill kernel's split-K partial sums (grids with
+ *    few tiles).  Each is allocated with hipMalloc on the first call that
+ *    needs it (at least 32 MiB), grown when a larger one is needed (after a
+ *    device synchronise) and held until process exit.  Calls that overlap in
+ *    time on one device (several streams or host threads) must not both use
+ *    them -- serialise them -- and the first such call must not be made
+ *    inside HIP stream capture.
  *  - Errors: every argument is validated BEFORE any HIP call; a failed check
  *    returns its status and enqueues nothing.  No call aborts or throws across
  *    the ABI.  HIP failures (including launch failures seen through
