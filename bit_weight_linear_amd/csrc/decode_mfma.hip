@@ -183,7 +183,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_mfma_kernel(
     b1 = to_f32(pre[kc + 1]);
     if (k >= K) b0 = b1 = 0.f;
   }
-  const float post_c = (post ? to_f32(post[min(n0 + 16 * wave + j, N - 1)]) : 1.f);
+  const float post_c = scale_or_one(post, min(n0 + 16 * wave + j, N - 1), W);   // W: >= 4N bytes
 
   // ---- 4. Remaining LDS writes, then one barrier.
   if constexpr (MODE != MODE_S3 && !FAST) {
@@ -335,17 +335,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= MN) return;
   const int64_t n = e % N;
-  const float s = (post ? to_f32(post[n]) : 1.f);
+  const float s = scale_or_one(post, n, partials);   // partials: >= MN floats
+  // Slices in batches of 8 (clamped indexes, masked terms): every load of a
+  // batch is in flight together, also for slice counts that are not a multiple
+  // of 8 (a plain tail loop would wait once per slice).
   float acc = 0.f;
-  int sl = 0;
-  for (; sl + 8 <= nslices; sl += 8) {
+  for (int s0 = 0; s0 < nslices; s0 += 8) {
     float v[8];
+    bool ok[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = partials[(int64_t)(sl + u) * MN + e];
+    for (int u = 0; u < 8; ++u) {
+      ok[u] = s0 + u < nslices;
+      v[u] = partials[(int64_t)(ok[u] ? s0 + u : 0) * MN + e];
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
+    for (int u = 0; u < 8; ++u) acc += ok[u] ? v[u] : 0.f;
   }
-  for (; sl < nslices; ++sl) acc += partials[(int64_t)sl * MN + e];
   Store<YT>::put(&Y[e], acc * s);
 }
 

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(
 #pragma unroll
   for (int j = 0; j < GM_FN; ++j) {
     const int64_t n = n0 + wn * (GM_FN * 16) + j * 16 + (lane & 15);
-    post_c[j] = (post ? to_f32(post[n < N ? n : N - 1]) : 1.f);
+    post_c[j] = scale_or_one(post, n < N ? n : N - 1, W);   // W: >= 4N bytes
   }
 
   Stager<AMODE, XT, ST, PRE> st;
@@ -431,7 +431,7 @@ void gemm_bf16_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
 
   // Prologue: side data of stage 0, output scales, DMA of stage 0.
   G.load_side(0);
-  if (tid < G2_BN) post_s[tid] = (post ? to_f32(post[min(G.n0 + tid, N - 1)]) : 1.f);
+  if (tid < G2_BN) post_s[tid] = scale_or_one(post, min(G.n0 + tid, N - 1), W);   // W: >= 4N bytes
   G.store_side(wsa, maga);
   G.dma(xa, 0);
 

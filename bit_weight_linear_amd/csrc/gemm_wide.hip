@@ -220,7 +220,7 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   dma(xb, wb, min(1, nk - 1));
 
   // Output scales of this tile, while stages 0 and 1 are in flight.
-  for (int c = tid; c < GW_BN; c += GW_THREADS) post_s[c] = (post ? to_f32(post[min(bn0 + c, N - 1)]) : 1.f);
+  for (int c = tid; c < GW_BN; c += GW_THREADS) post_s[c] = scale_or_one(post, min(bn0 + c, N - 1), W);
   __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): stages 0 and 1 landed
   __syncthreads();
 
@@ -367,9 +367,12 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   if (e0 >= MN) return;
   const int64_t n0 = e0 % N;
-  float acc[V];
+  float sc[V], acc[V];
 #pragma unroll
-  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  for (int e = 0; e < V; ++e) {
+    sc[e] = scale_or_one(post, n0 + e, part);   // part: >= MN floats; issued before the partial loads
+    acc[e] = 0.f;
+  }
   for (int s0 = 0; s0 < nsplit; s0 += 8) {
     float p[8][V];
     bool ok[8];
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
   }
 #pragma unroll
   for (int e = 0; e < V; ++e) {
-    const float y = acc[e] * (post ? to_f32(post[n0 + e]) : 1.f);
+    const float y = acc[e] * sc[e];
     Store<YT>::put(&Y[e0 + e], y);
     if (Y2) Store<bf16_t>::put(&Y2[e0 + e], y);
   }

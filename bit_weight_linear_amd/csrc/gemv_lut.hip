@@ -91,7 +91,7 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
 #pragma unroll
   for (int r = 0; r < RPH; ++r) {
     const int row = hw + LUT_HALFWAVES * r;
-    post_r[r] = (post ? to_f32(post[row0 + (row < nrows ? row : nrows - 1)]) : 1.f);
+    post_r[r] = scale_or_one(post, row0 + (row < nrows ? row : nrows - 1), W);   // W: >= 4N bytes
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
   }
@@ -173,16 +173,18 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
       }
     }
     lds_barrier();  // table visible; sign loads may still be in flight
-    // Pin every row's sign load above this point (otherwise the compiler sinks
-    // the loads of rows only some half-waves have into their conditional
-    // blocks, i.e. after the table build); the wait for the data lands here.
-#pragma unroll
-    for (int r = 0; r < RPH; ++r) asm volatile("" : "+v"(wv[r]));
 
-    // Lookups: one nibble -> one signed 4-term sum per input row.
+    // Lookups: one nibble -> one signed 4-term sum per input row.  Each row's
+    // sign load is pinned (an empty asm that takes the register) just before
+    // its own lookups and outside their condition: the pin stops the compiler
+    // from sinking the load into the conditional block (i.e. after the table
+    // build), and the wait for row r's data lands only there, so a wave starts
+    // on its first row while its later rows are still arriving (the CU returns
+    // loads in issue order, staggered across waves).
     const int cbase = 33 * c;
 #pragma unroll
     for (int r = 0; r < RPH; ++r) {
+      asm volatile("" : "+v"(wv[r]));
       if (hw + LUT_HALFWAVES * r < nrows) {
         const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
 #pragma unroll

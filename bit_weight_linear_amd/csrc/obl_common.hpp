@@ -51,6 +51,18 @@ template <> struct Store<f16_t> {
   }
 };
 
+// Element i of an optional scale vector, or 1 when it is absent (p null).
+// The load is issued unconditionally -- from `safe`, any buffer holding at
+// least i + 1 elements' worth of bytes, when p is null -- and the result is
+// selected: a load under a branch is waited for at the end of the branch,
+// which would put a memory round trip in front of every later load.
+template <typename ST>
+__device__ __forceinline__ float scale_or_one(const ST* p, int64_t i, const void* safe) {
+  const ST* q = p ? p : static_cast<const ST*>(safe);
+  const float v = to_f32(q[i]);
+  return p ? v : 1.f;
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's 16 bytes land at lds_wave_base + 16*l, where lds_wave_base must be
 // the same for the whole wave.  Counted by vmcnt like any vector load.
