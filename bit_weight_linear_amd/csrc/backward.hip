@@ -47,7 +47,9 @@ __global__ __launch_bounds__(256) void transpose_signs_kernel(const uint32_t* __
 
 // Gradient reduction.  Blocks [0, bk) own 64 columns k of dX / db, blocks
 // [bk, bk + bn) own 64 columns j of da.  Wave w of a block sums rows
-// i = w, w + 4, ...; the four wave partials are added in wave order in LDS
+// i = w, w + 4, ..., eight rows per batch: the batch's loads are issued
+// together (row indexes clamped, terms masked) so a wave waits once per batch,
+// not once per row.  The four wave partials are added in wave order in LDS
 // (fixed order: bitwise reproducible).
 template <typename XT, typename ST, typename DT>
 __global__ __launch_bounds__(256) void backward_grads_kernel(
@@ -63,16 +65,41 @@ __global__ __launch_bounds__(256) void backward_grads_kernel(
   if ((int)blockIdx.x < bk) {
     col = (int64_t)blockIdx.x * 64 + lane;
     ok = col < K;
-    const float bk_s = ok ? to_f32(b[col]) : 0.f;
-    for (int64_t i = wave; i < M && ok; i += 4) {
-      const float u = U[i * K + col];
-      acc += to_f32(X[i * K + col]) * u;
-      Store<DT>::put(&dX[i * K + col], u * bk_s);
+    const int64_t cc = ok ? col : K - 1;
+    const float bk_s = to_f32(b[cc]);
+    for (int64_t i0 = wave; i0 < M; i0 += 4 * 8) {
+      float u[8], x[8];
+      bool okr[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        okr[r] = i0 + 4 * r < M;
+        const int64_t i = okr[r] ? i0 + 4 * r : wave;   // row `wave` exists when the loop runs
+        u[r] = U[i * K + cc];
+        x[r] = to_f32(X[i * K + cc]);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        acc += okr[r] ? x[r] * u[r] : 0.f;
+        if (okr[r] && ok) Store<DT>::put(&dX[(i0 + 4 * r) * K + col], u[r] * bk_s);
+      }
     }
   } else {
     col = (int64_t)(blockIdx.x - bk) * 64 + lane;
     ok = col < N;
-    for (int64_t i = wave; i < M && ok; i += 4) acc += to_f32(dY[i * N + col]) * T[i * N + col];
+    const int64_t cc = ok ? col : N - 1;
+    for (int64_t i0 = wave; i0 < M; i0 += 4 * 8) {
+      float g[8], t[8];
+      bool okr[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        okr[r] = i0 + 4 * r < M;
+        const int64_t i = okr[r] ? i0 + 4 * r : wave;
+        g[r] = to_f32(dY[i * N + cc]);
+        t[r] = T[i * N + cc];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc += okr[r] ? g[r] * t[r] : 0.f;
+    }
   }
   part[wave][lane] = acc;
   __syncthreads();

@@ -110,6 +110,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_b
 
 constexpr int GW_XDMA = GW_BM * (GW_KT / 8) / 64 / 4;    // activation DMAs per wave per stage (8)
 constexpr int GW_WCOLS = 512;                             // sign columns staged (>= GW_BN, 2 DMAs per wave)
+constexpr int GW_BTAB_BATCH = 8 * GW_THREADS;             // bf16(b) pairs per table-fill batch
+static_assert(GW_BN <= 2 * GW_THREADS, "two output scales per thread");
+
+// Entries of the bf16(b) pair table: K / 2 rounded up to whole fill batches.
+inline int64_t gw_btab_entries(int64_t K) {
+  return (K / 2 + GW_BTAB_BATCH - 1) / GW_BTAB_BATCH * GW_BTAB_BATCH;
+}
 constexpr int GW_WDMA = GW_WCOLS / 64 / 4;                // sign DMAs per wave per stage (2)
 
 // SPLIT: block b takes tile b / nsplit and the 128-k stages
@@ -131,8 +138,8 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   __shared__ u32x4 wa[GW_WCOLS];             // 4 packed words (128 k) per column
   __shared__ u32x4 wb[GW_WCOLS];
   __shared__ u32x4 wc[GW_WCOLS];
-  __shared__ float post_s[GW_BN];
-  extern __shared__ uint32_t btab[];         // [K / 2] bf16(b) pairs (with b only)
+  __shared__ float post_s[2 * GW_THREADS];   // GW_BN used
+  extern __shared__ uint32_t btab[];         // [gw_btab_entries(K)] bf16(b) pairs (with b only)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,25 +157,6 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(N * kw * 4));
 
-  // The bf16(b) table, once per workgroup: all loads of a batch are issued
-  // before any is used.
-  if constexpr (PRE) {
-    const int64_t npair = K / 2;
-    for (int64_t p0 = 0; p0 < npair; p0 += 8 * GW_THREADS) {
-      float lo[8], hi[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t pc = min(p0 + u * GW_THREADS + tid, npair - 1);
-        lo[u] = to_f32(pre[2 * pc]);
-        hi[u] = to_f32(pre[2 * pc + 1]);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t pp = p0 + u * GW_THREADS + tid;
-        if (pp < npair) btab[pp] = pack_bf16_pair(lo[u], hi[u]);
-      }
-    }
-  }
 
   // Shift pairs: dword j of half-group g takes bits 8g + 2j (-> 15) and
   // 8g + 2j + 1 (-> 31) of a 16-bit half.
@@ -219,8 +207,39 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   dma(xa, wa, 0);
   dma(xb, wb, min(1, nk - 1));
 
-  // Output scales of this tile, while stages 0 and 1 are in flight.
-  for (int c = tid; c < GW_BN; c += GW_THREADS) post_s[c] = scale_or_one(post, min(bn0 + c, N - 1), W);
+  // Output scales of this tile (loads issued now, stored below), then the
+  // bf16(b) table, all while stages 0 and 1 are in flight.
+  float ps0 = 1.f, ps1 = 1.f;
+  if constexpr (!SPLIT) {
+    ps0 = scale_or_one(post, min(bn0 + tid, N - 1), W);
+    ps1 = scale_or_one(post, min(bn0 + tid + GW_THREADS, N - 1), W);
+  }
+
+  // The table is filled after the stage DMAs are issued: the CU returns
+  // loads in issue order, so waiting for its inputs also covers the two
+  // stages (one round trip for both).  All loads of a batch are issued before
+  // any is used, and the stores are unconditional (the table is padded to
+  // whole batches, see gw_btab_entries): a store under a branch takes its
+  // load into the branch, where it is waited for at once.
+  if constexpr (PRE) {
+    const int64_t npair = K / 2;
+    for (int64_t p0 = 0; p0 < npair; p0 += GW_BTAB_BATCH) {
+      float lo[8], hi[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t pc = min(p0 + u * GW_THREADS + tid, npair - 1);
+        lo[u] = to_f32(pre[2 * pc]);
+        hi[u] = to_f32(pre[2 * pc + 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) btab[p0 + u * GW_THREADS + tid] = pack_bf16_pair(lo[u], hi[u]);
+    }
+  }
+
+  if constexpr (!SPLIT) {                  // padded: GW_BN <= 2 * GW_THREADS
+    post_s[tid] = ps0;
+    post_s[tid + GW_THREADS] = ps1;
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): stages 0 and 1 landed
   __syncthreads();
 
@@ -417,7 +436,7 @@ hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
   const int64_t nt = (a.N + GW_BN - 1) / GW_BN;
   const int64_t tiles = mt * nt;
   const int64_t nk = a.K / GW_KT;
-  const size_t lds = (PRE ? a.K / 2 : 0) * sizeof(uint32_t);
+  const size_t lds = (PRE ? gw_btab_entries(a.K) : 0) * sizeof(uint32_t);
   int nsplit = split_count(tiles, nk, dev.num_cus);
   if (nsplit > 1) {
     const int per = (int)((nk + nsplit - 1) / nsplit);
@@ -472,8 +491,8 @@ bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const voi
   if (a.M * a.K * 2 > lim || a.N * (a.K / 32) * 4 > lim) return false;
   const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GW_BN - 1) / GW_BN);
   if (tiles > 0x7fffffff) return false;
-  // LDS: the bf16(b) table (2K bytes, dynamic) next to 122 KiB of static
-  // stage buffers.
+  // LDS: the bf16(b) table (2K bytes rounded up to 8 KiB batches, dynamic)
+  // next to ~124 KiB of static stage buffers.
   return !a.pre || a.K <= 16384;
 }
 
