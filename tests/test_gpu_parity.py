@@ -193,6 +193,17 @@ def test_workload5_dbf():
     assert r1 <= G.TOL_DECODE and r2 <= G.TOL_DECODE and r <= G.TOL_DECODE
 
 
+@pytest.mark.parametrize("path,M", [("lut", 1), ("lut", 2), ("decode", 16), ("gemm", 64), ("gemm", 300)])
+def test_long_k(path, M):
+    """K = 20480: several GEMV slabs, 40 decode slices, and for the GEMM a K
+    whose bf16(b) table no longer fits next to the main kernel's stage
+    buffers (the prefill path falls back to the LDS-staged kernel)."""
+    K, N = 20480, 300
+    G.say(f"long K {path} M={M} K={K} N={N}")
+    c = WL.onebit_case(M, K, N, seed=M + 7)
+    G.check_onebit(c, G.run_onebit(c, path), path)
+
+
 # ------------------------------------------------------------------ exact regimes
 @pytest.mark.parametrize("path,M,K,N", [("lut", 1, 4096, 1000), ("lut", 2, 8224, 77),
                                         ("decode", 16, 4096, 4096), ("decode", 9, 544, 65),
