@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <new>
 #include <unordered_map>
@@ -51,6 +52,15 @@ bool overlap(Range a, Range b) {
 }
 
 bool aligned(const void* p, int64_t n) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)n) == 0; }
+
+// Every dimension must fit in int32: kernel grids and per-block row counts are
+// derived from them in 32 bits.
+constexpr int64_t kMaxDim = 0x7fffffff;
+bool dims_ok(std::initializer_list<int64_t> dims) {
+  for (int64_t d : dims)
+    if (d > kMaxDim) return false;
+  return true;
+}
 
 // Path selection.  OBL_PATH=lut|decode|gemm forces a path (tests use this to
 // cover every kernel at every M it supports); unset or "auto" picks by M.
@@ -212,7 +222,7 @@ obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_
                           uint32_t* packed, void* stream) {
   try {
     if (!S || !packed) return OBL_ERR_NULL;
-    if (rows < 1 || K < 1 || K % 32 != 0) return OBL_ERR_SHAPE;
+    if (rows < 1 || K < 1 || K % 32 != 0 || !dims_ok({rows, K})) return OBL_ERR_SHAPE;
     if (!valid_dtype(s_dtype)) return OBL_ERR_DTYPE;
     int64_t sb = checked_bytes(rows, K, elem_size(s_dtype));
     int64_t pb = checked_bytes(rows, K / 32, 4);
@@ -232,7 +242,7 @@ obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const void* a, const void* b, obl_dtype scale_dtype,
                       void* Y, obl_dtype y_dtype, void* stream) {
   try {
-    if (M < 0 || K < 1 || N < 1 || K % 32 != 0) return OBL_ERR_SHAPE;
+    if (M < 0 || K < 1 || N < 1 || K % 32 != 0 || !dims_ok({M, K, N})) return OBL_ERR_SHAPE;
     if (!W_packed || !a || !b) return OBL_ERR_NULL;
     if (M > 0 && (!X || !Y)) return OBL_ERR_NULL;
     if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(y_dtype))
@@ -265,7 +275,7 @@ obl_status obl_svid(const void* W, obl_dtype w_dtype, int64_t N, int64_t K, int 
                     void* a, void* b, obl_dtype scale_dtype, void* stream) {
   try {
     if (!W || !packed || !a || !b) return OBL_ERR_NULL;
-    if (N < 1 || K < 1 || K % 32 != 0 || iters < 1 || iters > 100000) return OBL_ERR_SHAPE;
+    if (N < 1 || K < 1 || K % 32 != 0 || iters < 1 || iters > 100000 || !dims_ok({N, K})) return OBL_ERR_SHAPE;
     if (w_dtype != OBL_F32 && w_dtype != OBL_F16 && w_dtype != OBL_BF16) return OBL_ERR_DTYPE;
     if (scale_dtype != OBL_F32 && scale_dtype != OBL_F16) return OBL_ERR_DTYPE;
     const int ws = elem_size(w_dtype), ss = elem_size(scale_dtype);
@@ -298,7 +308,7 @@ obl_status obl_transpose_signs(const uint32_t* packed, int64_t rows, int64_t K, 
                                void* stream) {
   try {
     if (!packed || !packed_t) return OBL_ERR_NULL;
-    if (rows < 1 || K < 1 || K % 32 != 0 || rows % 32 != 0) return OBL_ERR_SHAPE;
+    if (rows < 1 || K < 1 || K % 32 != 0 || rows % 32 != 0 || !dims_ok({rows, K})) return OBL_ERR_SHAPE;
     int64_t pb = checked_bytes(rows, K / 32, 4), tb = checked_bytes(K, rows / 32, 4);
     if (pb < 0 || tb < 0) return OBL_ERR_SHAPE;
     if (!aligned(packed, 4) || !aligned(packed_t, 4)) return OBL_ERR_ALIGN;
@@ -317,7 +327,7 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
                                void* dX, obl_dtype dx_dtype, float* da, float* db,
                                float* workspace, void* stream) {
   try {
-    if (M < 0 || K < 1 || N < 1 || K % 32 != 0 || N % 32 != 0) return OBL_ERR_SHAPE;
+    if (M < 0 || K < 1 || N < 1 || K % 32 != 0 || N % 32 != 0 || !dims_ok({M, K, N})) return OBL_ERR_SHAPE;
     if (!W_packed || !Wt_packed || !a || !b || !da || !db) return OBL_ERR_NULL;
     if (M > 0 && (!dY || !X || !dX || !workspace)) return OBL_ERR_NULL;
     if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(dx_dtype))
@@ -377,7 +387,7 @@ obl_status obl_layernorm(const void* Y, obl_dtype y_dtype, int64_t M, int64_t N,
                          const void* gamma, const void* beta, obl_dtype affine_dtype,
                          void* Z, obl_dtype z_dtype, void* stream) {
   try {
-    if (M < 0 || N < 1) return OBL_ERR_SHAPE;
+    if (M < 0 || N < 1 || !dims_ok({M, N})) return OBL_ERR_SHAPE;
     if (M > 0 && !Y) return OBL_ERR_NULL;
     if (!valid_dtype(y_dtype) || (y_dtype != OBL_F32 && y_dtype != OBL_BF16)) return OBL_ERR_DTYPE;
     const int ys = elem_size(y_dtype);
@@ -403,7 +413,7 @@ obl_status obl_linear_layernorm(const void* X, obl_dtype x_dtype, int64_t M, int
                                 float eps, const void* gamma, const void* beta,
                                 float* workspace, void* Z, obl_dtype z_dtype, void* stream) {
   try {
-    if (M < 0 || K < 1 || N < 1 || K % 32 != 0) return OBL_ERR_SHAPE;
+    if (M < 0 || K < 1 || N < 1 || K % 32 != 0 || !dims_ok({M, K, N})) return OBL_ERR_SHAPE;
     if (!W_packed || !a || !b) return OBL_ERR_NULL;
     if (M > 0 && (!X || !workspace)) return OBL_ERR_NULL;
     if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype)) return OBL_ERR_DTYPE;
@@ -446,7 +456,8 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const void* b, const void* m, const void* a, obl_dtype scale_dtype,
                       float* workspace, void* Y, obl_dtype y_dtype, void* stream) {
   try {
-    if (M < 0 || K < 1 || Kmid < 1 || N < 1 || K % 32 != 0 || Kmid % 32 != 0) return OBL_ERR_SHAPE;
+    if (M < 0 || K < 1 || Kmid < 1 || N < 1 || K % 32 != 0 || Kmid % 32 != 0 || !dims_ok({M, K, Kmid, N}))
+      return OBL_ERR_SHAPE;
     if (!S2_packed || !S1_packed || !b || !m || !a) return OBL_ERR_NULL;
     if (M > 0 && (!X || !Y || !workspace)) return OBL_ERR_NULL;
     if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(y_dtype))

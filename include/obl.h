@@ -38,8 +38,8 @@
  *    hipGetLastError) return OBL_ERR_HIP.
  *  - M = 0 is a valid no-op.  N, K, Kmid, rows must be >= 1 and K, Kmid must
  *    be multiples of 32 (the packed word width); a call that violates this
- *    returns OBL_ERR_SHAPE.  Dimensions must also keep every byte size below
- *    2^62.
+ *    returns OBL_ERR_SHAPE.  Every dimension must be below 2^31 and keep every
+ *    byte size below 2^62 (else OBL_ERR_SHAPE).
  */
 #ifndef OBL_H_
 #define OBL_H_

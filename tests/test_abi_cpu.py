@@ -67,6 +67,9 @@ def test_linear_valid_m0_is_noop():
     (dict(K=100), b.OBL_ERR_SHAPE),
     (dict(N=0), b.OBL_ERR_SHAPE),
     (dict(M=1 << 40, K=1 << 30), b.OBL_ERR_SHAPE),
+    (dict(M=1 << 31, K=32, N=1), b.OBL_ERR_SHAPE),          # dimension beyond int32
+    (dict(M=1, K=1 << 31, N=1), b.OBL_ERR_SHAPE),
+    (dict(M=1, K=32, N=1 << 31), b.OBL_ERR_SHAPE),
     (dict(xd=b.OBL_I8), b.OBL_ERR_DTYPE),
     (dict(xd=b.OBL_F16), b.OBL_ERR_DTYPE),
     (dict(sd=b.OBL_BF16), b.OBL_ERR_DTYPE),
@@ -211,6 +214,8 @@ def test_layernorm_m0_is_noop():
     (dict(M=-1), b.OBL_ERR_SHAPE),
     (dict(N=0), b.OBL_ERR_SHAPE),
     (dict(M=1 << 40, N=1 << 30), b.OBL_ERR_SHAPE),
+    (dict(M=1 << 31, N=1), b.OBL_ERR_SHAPE),
+    (dict(M=1, N=1 << 31), b.OBL_ERR_SHAPE),
     (dict(yd=b.OBL_F16), b.OBL_ERR_DTYPE),
     (dict(zd=b.OBL_I8), b.OBL_ERR_DTYPE),
     (dict(gd=b.OBL_BF16), b.OBL_ERR_DTYPE),
@@ -260,3 +265,16 @@ def test_linear_layernorm_m0_is_noop():
 ])
 def test_linear_layernorm_rejects(kw, code):
     assert lln(**kw) == code
+
+
+def test_every_call_rejects_dimensions_beyond_int32():
+    big = 1 << 31
+    assert L.obl_pack_signs(X, b.OBL_I8, big, 32, W, None) == b.OBL_ERR_SHAPE
+    assert L.obl_transpose_signs(W, big, 32, Y, None) == b.OBL_ERR_SHAPE
+    assert L.obl_svid(X, b.OBL_F16, big, 32, 4, W, A, B_, b.OBL_F16, None) == b.OBL_ERR_SHAPE
+    assert L.dbf_linear(X, b.OBL_BF16, 1, 32, W, big, S1, 32, A, B_, Y, b.OBL_F16, WS, P(0x80_0000_0000),
+                        b.OBL_F32, None) == b.OBL_ERR_SHAPE
+    assert L.obl_linear_backward(X, Y, b.OBL_BF16, 1, 32, W, S1, big, A, B_, b.OBL_F16, WS, b.OBL_F32,
+                                 P(0x80_0000_0000), P(0x90_0000_0000), P(0xA0_0000_0000), None) == b.OBL_ERR_SHAPE
+    assert L.obl_linear_layernorm(X, b.OBL_BF16, big, 32, W, 32, A, B_, b.OBL_F16, 1e-5, None, None, WS, Y,
+                                  b.OBL_F32, None) == b.OBL_ERR_SHAPE
