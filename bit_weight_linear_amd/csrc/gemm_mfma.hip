@@ -568,6 +568,7 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
                   (!a.pre || (a.scale_dtype == DT_F16 && reinterpret_cast<uintptr_t>(a.pre) % 16 == 0));
   const int forced = gemm_forced();
   if (forced == 0 && gemm_wide_eligible(a)) return launch_gemm_wide(a, dev);
+  if (forced == 0 && gemm_wide_prescale_eligible(a)) return launch_gemm_wide_prescaled(a, dev);
   if (a.Y2) return hipErrorInvalidValue;   // only the wide kernel writes the bf16 copy
   if (v2 && forced != 1) {
     if constexpr (std::is_same<ST, f16_t>::value) {

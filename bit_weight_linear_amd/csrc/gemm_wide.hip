@@ -473,7 +473,85 @@ hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
   return a.pre ? launch<ST, bf16_t, true>(a, dev) : launch<ST, bf16_t, false>(a, dev);
 }
 
+// X'[m][k] = bf16(x_mk · b_k) (or bf16(x_mk) without b): the activations of
+// the prescaled route, one rounding of the input-side product as the fp32
+// staging of the other kernels does.  VEC = 4 when X (and b) allow 4-element
+// loads; K % 4 == 0 keeps a vector inside one row.  Grid-stride.
+template <typename XT, typename ST, bool PRE, int VEC>
+__global__ __launch_bounds__(256) void prescale_kernel(const XT* __restrict__ X, int64_t total, int64_t K,
+                                                       const ST* __restrict__ pre, bf16_t* __restrict__ Xp) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < total; e += stride) {
+    const int64_t k = e % K;
+    float x[4], b[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (VEC == 4) {
+      if constexpr (sizeof(XT) == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(X + e);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(X + e);
+        x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = to_f32(X[e + i]);
+    }
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = to_f32(pre[k + i]);
+    }
+    *reinterpret_cast<u32x2*>(Xp + e) = u32x2{pack_bf16_pair(x[0] * b[0], x[1] * b[1]),
+                                              pack_bf16_pair(x[2] * b[2], x[3] * b[3])};
+  }
+}
+
+template <typename XT, typename ST, bool PRE>
+void launch_prescale(const LinearArgs& a, bf16_t* Xp) {
+  const int64_t total = a.M * a.K;
+  const int64_t blocks = std::min<int64_t>((total / 4 + 255) / 256, 4096);
+  const bool vec = reinterpret_cast<uintptr_t>(a.X) % (4 * sizeof(XT)) == 0;
+  if (vec)
+    hipLaunchKernelGGL((prescale_kernel<XT, ST, PRE, 4>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const XT*>(a.X), total, a.K, static_cast<const ST*>(a.pre), Xp);
+  else
+    hipLaunchKernelGGL((prescale_kernel<XT, ST, PRE, 1>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const XT*>(a.X), total, a.K, static_cast<const ST*>(a.pre), Xp);
+}
+
+template <typename XT, typename ST>
+void launch_prescale_p(const LinearArgs& a, bf16_t* Xp) {
+  if (a.pre) launch_prescale<XT, ST, true>(a, Xp);
+  else launch_prescale<XT, ST, false>(a, Xp);
+}
+
 }  // namespace
+
+bool gemm_wide_prescale_eligible(const LinearArgs& a) {
+  if (a.Y2) return false;
+  // The prescaled activations live in 256-byte aligned scratch: only K, N, W
+  // and the sizes matter (no input-side table).
+  return gemm_wide_shape_ok(a.M, a.K, a.N, false, a.W, a.W);
+}
+
+hipError_t launch_gemm_wide_prescaled(const LinearArgs& a, const DeviceInfo& dev) {
+  Scratch sc{};
+  hipError_t e = scratch_reserve(dev.device, (size_t)((a.M * a.K + 1) / 2 + 64), &sc);
+  if (e != hipSuccess) return e;
+  bf16_t* Xp = reinterpret_cast<bf16_t*>(sc.partials);
+  if (a.x_dtype == DT_F32) {
+    if (a.scale_dtype == DT_F32) launch_prescale_p<float, float>(a, Xp);
+    else launch_prescale_p<float, f16_t>(a, Xp);
+  } else {
+    if (a.scale_dtype == DT_F32) launch_prescale_p<bf16_t, float>(a, Xp);
+    else launch_prescale_p<bf16_t, f16_t>(a, Xp);
+  }
+  LinearArgs b = a;
+  b.X = Xp;
+  b.x_dtype = DT_BF16;
+  b.pre = nullptr;
+  return launch_gemm_wide(b, dev);
+}
 
 bool gemm_wide_eligible(const LinearArgs& a) {
   if (a.x_dtype != DT_BF16) return false;

@@ -58,6 +58,11 @@ bool gemm_wide_eligible(const LinearArgs& a);
 // Shape/alignment test for a bf16-activation prefill call of the given sizes.
 bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const void* X, const void* W);
 hipError_t launch_gemm_wide(const LinearArgs& a, const DeviceInfo& dev);
+// Prefill for activations the main kernel cannot take directly (fp32, or bf16
+// that is misaligned or whose b exceeds the table): bf16(x ⊙ b) into library
+// scratch (the first buffer), then the main kernel without b.
+bool gemm_wide_prescale_eligible(const LinearArgs& a);
+hipError_t launch_gemm_wide_prescaled(const LinearArgs& a, const DeviceInfo& dev);
 
 // Largest M served by the LUT GEMV and by the decode kernel.
 constexpr int64_t kLutMaxM = 2;

@@ -24,9 +24,10 @@
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer
  *    to caller memory after a call returns.  It keeps two scratch buffers per
  *    device: one for the decode kernels' split-K partial sums (M <= 16), the
- *    bf16 copy of the DBF intermediate at prefill sizes and the vectors of
- *    obl_svid, one for the prefill kernel's split-K partial sums (grids with
- *    few tiles).  Each is allocated with hipMalloc on the first call that
+ *    bf16 copy of the DBF intermediate at prefill sizes, the bf16(x ⊙ b)
+ *    activations the prefill path stages for fp32 or misaligned X, and the
+ *    vectors of obl_svid; one for the prefill kernel's split-K partial sums
+ *    (grids with few tiles).  Each is allocated with hipMalloc on the first call that
  *    needs it (at least 32 MiB), grown when a larger one is needed (after a
  *    device synchronise) and held until process exit.  Calls that overlap in
  *    time on one device (several streams or host threads) must not both use
