@@ -475,47 +475,58 @@ hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
 
 // X'[m][k] = bf16(x_mk · b_k) (or bf16(x_mk) without b): the activations of
 // the prescaled route, one rounding of the input-side product as the fp32
-// staging of the other kernels does.  VEC = 4 when X (and b) allow 4-element
-// loads; K % 4 == 0 keeps a vector inside one row.  Grid-stride.
-template <typename XT, typename ST, bool PRE, int VEC>
+// staging of the other kernels does.  Eight consecutive elements per thread
+// (K % 128 == 0 keeps them inside one row), 16-byte stores; VEC loads where X
+// allows them.  The grid covers the matrix once for the usual sizes; the
+// stride loop only serves larger ones.
+template <typename XT, typename ST, bool PRE, bool VEC>
 __global__ __launch_bounds__(256) void prescale_kernel(const XT* __restrict__ X, int64_t total, int64_t K,
                                                        const ST* __restrict__ pre, bf16_t* __restrict__ Xp) {
-  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
-  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < total; e += stride) {
-    const int64_t k = e % K;
-    float x[4], b[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (VEC == 4) {
-      if constexpr (sizeof(XT) == 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(X + e);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-      } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(X + e);
-        x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xFFFF0000u);
-        x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; e < total; e += stride) {
+    float x[8], b[8];
+    if constexpr (VEC && sizeof(XT) == 4) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(X + e);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(X + e + 4);
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    } else if constexpr (VEC) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(X + e);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = to_f32(X[e + i]);
+      for (int i = 0; i < 8; ++i) x[i] = to_f32(X[e + i]);
     }
     if constexpr (PRE) {
+      const int64_t k = e % K;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = to_f32(pre[k + i]);
+      for (int i = 0; i < 8; ++i) b[i] = to_f32(pre[k + i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = 1.f;
     }
-    *reinterpret_cast<u32x2*>(Xp + e) = u32x2{pack_bf16_pair(x[0] * b[0], x[1] * b[1]),
-                                              pack_bf16_pair(x[2] * b[2], x[3] * b[3])};
+    *reinterpret_cast<u32x4*>(Xp + e) = u32x4{pack_bf16_pair(x[0] * b[0], x[1] * b[1]),
+                                              pack_bf16_pair(x[2] * b[2], x[3] * b[3]),
+                                              pack_bf16_pair(x[4] * b[4], x[5] * b[5]),
+                                              pack_bf16_pair(x[6] * b[6], x[7] * b[7])};
   }
 }
 
 template <typename XT, typename ST, bool PRE>
 void launch_prescale(const LinearArgs& a, bf16_t* Xp) {
   const int64_t total = a.M * a.K;
-  const int64_t blocks = std::min<int64_t>((total / 4 + 255) / 256, 4096);
-  const bool vec = reinterpret_cast<uintptr_t>(a.X) % (4 * sizeof(XT)) == 0;
+  const int64_t blocks = std::min<int64_t>((total / 8 + 255) / 256, 65536);
+  const bool vec = reinterpret_cast<uintptr_t>(a.X) % 16 == 0;
   if (vec)
-    hipLaunchKernelGGL((prescale_kernel<XT, ST, PRE, 4>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((prescale_kernel<XT, ST, PRE, true>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const XT*>(a.X), total, a.K, static_cast<const ST*>(a.pre), Xp);
   else
-    hipLaunchKernelGGL((prescale_kernel<XT, ST, PRE, 1>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((prescale_kernel<XT, ST, PRE, false>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const XT*>(a.X), total, a.K, static_cast<const ST*>(a.pre), Xp);
 }
 
