@@ -222,10 +222,16 @@ def cpu_baseline(WL, O, budget_s: float = 12.0):
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     wbytes = c.N * c.K / 8
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": round(wbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(times)} full calls of workload 1x4096x11008 (fp64 dense W = W_sign*(a b^T) "
                       f"then X W^T), median {t * 1e3:.1f} ms per call; weight bytes N*K/8 per call; "
-                      f"dense-W formation is single-threaded NumPy, the product uses {threads} BLAS threads"}
+                      f"dense-W formation is single-threaded NumPy, the product uses {threads} BLAS threads; "
+                      f"host os.cpu_count() = {os.cpu_count()}, affinity {affinity}, "
+                      f"OPENBLAS_NUM_THREADS = {os.environ.get('OPENBLAS_NUM_THREADS')}"}
 
 
 def main():
@@ -319,8 +325,13 @@ def main():
             ti = Timed(torch, li)
             _, msi = ti.run(args.warmup, args.steps)
             wb = ci.N * ci.K / 8
+            ab = (wb + ci.M * ci.K * (4 if ci.x_dtype == "f32" else 2)
+                  + (ci.N + ci.K) * (4 if ci.scale_dtype == "f32" else 2) + ci.M * ci.N * 4)
             sec[ci.name] = {"us_per_launch": round(msi * 1e3, 3),
                             "weight_GBps": round(wb / (msi * 1e-3) / 1e9, 1),
+                            "algorithmic_bytes": int(ab), "ideal_us_hbm": round(ab / HBM_PEAK_GBS / 1e3, 4),
+                            "hbm_frac": round(ab / (msi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "bound": "latency (launch and one HBM round trip; the HBM time is a fraction of it)",
                             "parity_max_normalised_error": float(f"{ei:.3e}"), "copies": Ri}
             log(f"[bench] {ci.name}: {msi * 1e3:.2f} us")
             del li, ti
@@ -330,7 +341,11 @@ def main():
         t5 = Timed(torch, l5)
         _, ms5 = t5.run(args.warmup, args.steps)
         wb5 = c5.Kmid * (c5.K + c5.N) / 8
+        ab5 = wb5 + c5.M * c5.K * 2 + (c5.K + c5.Kmid + c5.N) * 2 + 2 * c5.M * c5.Kmid * 4 + c5.M * c5.N * 4
         sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
+                        "algorithmic_bytes": int(ab5), "ideal_us_hbm": round(ab5 / HBM_PEAK_GBS / 1e3, 4),
+                        "hbm_frac": round(ab5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "bound": "latency (two stages, four launches)",
                         "parity_max_normalised_error": float(f"{e5:.3e}"), "copies": R5,
                         "stages_per_call": 2}
         log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
