@@ -52,7 +52,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Both enums have int as their underlying type in C++ too, so that any
+ * integer a C caller passes (an invalid dtype, an unknown status) is a valid
+ * value to inspect and reject, not undefined behaviour. */
+#ifdef __cplusplus
+#define OBL_ENUM(tag) enum tag : int
+#else
+#define OBL_ENUM(tag) enum tag
+#endif
+
+typedef OBL_ENUM(obl_status_e) {
   OBL_OK = 0,
   OBL_ERR_NULL = 1,     /* a required pointer is NULL */
   OBL_ERR_SHAPE = 2,    /* a dimension is negative / zero where not allowed / not a multiple of 32 */
@@ -64,7 +73,7 @@ typedef enum {
   OBL_ERR_VALUE = 8     /* a scalar argument is out of range (e.g. a negative epsilon) */
 } obl_status;
 
-typedef enum {
+typedef OBL_ENUM(obl_dtype_e) {
   OBL_F32 = 0,
   OBL_F16 = 1,
   OBL_BF16 = 2,
