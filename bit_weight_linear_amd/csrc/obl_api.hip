@@ -216,7 +216,7 @@ const char* obl_status_string(obl_status s) {
   return "OBL_ERR_UNKNOWN";
 }
 
-int obl_version(void) { return 100; }  // 0.1.0
+int obl_version(void) { return 200; }  // 0.2.0: adds SVID, the backward, LayerNorm, int32 dimension limits
 
 obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_t K,
                           uint32_t* packed, void* stream) {
