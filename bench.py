@@ -14,8 +14,13 @@ with fp16 scales, fp32 output.
   + Y) / average launch time over the timed region (HIP events on the stream
   the graph replays on).
 * cpu_baseline = the fp64 oracle on the same workload, timed on the host.
-* secondary = the other workloads (prefill GEMM TOPS, batched decode, DBF),
-  timed the same way, parity-checked before timing.
+* secondary = the other workloads (prefill GEMM TOPS, batched decode, DBF, the
+  NEXT rows), timed the same way.
+* Before timing, every line's outputs are checked against a plain fp32 PyTorch
+  computation on the GPU: a guard against timing a broken configuration.  The
+  parity claims against the fp64 oracle belong to tests/ (each timed
+  configuration has a full-size parity test there); here the oracle only runs
+  in the cpu_baseline leg.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu-baseline]
 """
@@ -105,81 +110,95 @@ class Timed:
         return ms / steps, ms / (steps * self.n)   # ms per step, ms per launch
 
 
-def onebit_setup(torch, B, WL, O, i, rotate_bytes, check_rows=None, check_cols=None):
-    import numpy as np
+# ------------------------------------------------------------------ guards
+# Plain fp32 PyTorch on the GPU (allow_tf32 off); errors on the normalised scale
+# |a_j| Σ_k |x_ik b_k| (or its DBF product) as in the tests.
+def t_err(torch, Y, Yref, S):
+    d = (Y.double() - Yref.double()).abs()
+    S = S.double().expand_as(d)
+    r = torch.where(S > 0, d / S, torch.where(d > 0, torch.full_like(d, float("inf")), torch.zeros_like(d)))
+    return float(r.max())
+
+
+def t_linear(torch, X, Spm1, a, b):
+    """Y = ((X ⊙ b) S^T) ⊙ a in fp32 and its normalised scale."""
+    Xb = X.float() * b.float()[None, :]
+    Y = (Xb @ Spm1.float().t()) * a.float()[None, :]
+    S = Xb.abs().sum(1, keepdim=True) * a.float().abs()[None, :]
+    return Y, S
+
+
+def t_dbf(torch, X, S2, S1, b, m, a):
+    T1 = ((X.float() * b.float()[None, :]) @ S2.float().t()) * m.float()[None, :]
+    Y = (T1 @ S1.float().t()) * a.float()[None, :]
+    S = ((X.float() * b.float()[None, :]).abs().sum(1, keepdim=True) * m.float().abs().sum()
+         * a.float().abs()[None, :])
+    return Y, S
+
+
+def onebit_setup(torch, B, WL, i, rotate_bytes):
     c = WL.workload(i)
     dev = torch.device("cuda")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     X = torch.from_numpy(c.X).to(torch.float32).to(tdt[c.x_dtype]).to(dev)
     a0 = torch.from_numpy(c.a).to(torch.float32).to(tdt[c.scale_dtype]).to(dev)
     b0 = torch.from_numpy(c.b).to(torch.float32).to(tdt[c.scale_dtype]).to(dev)
-    W0 = B.pack_signs(torch.from_numpy(c.W_sign).to(dev))
-    torch.cuda.synchronize()
-    assert np.array_equal(W0.cpu().numpy().view(np.uint32), O.pack_signs(c.W_sign)), "pack mismatch"
+    Spm1 = torch.from_numpy(c.W_sign).to(dev)
+    W0 = B.pack_signs(Spm1)
     per_copy = W0.numel() * 4 + a0.numel() * a0.element_size() + b0.numel() * b0.element_size()
     R = max(1, -(-rotate_bytes // per_copy))
     copies = [(W0, a0, b0)] + [(W0.clone(), a0.clone(), b0.clone()) for _ in range(R - 1)]
     Y = torch.empty((c.M, c.N), dtype=tdt[c.y_dtype], device=dev)
-    # parity of the timed configuration on the first copy
+    # guard on the timed configuration, first copy
     B.linear(X, W0, a0, b0, out=Y)
-    torch.cuda.synchronize()
-    Yh = Y.float().cpu().numpy().astype(np.float64)
-    rows = np.arange(c.M) if check_rows is None else check_rows
-    cols = np.arange(c.N) if check_cols is None else check_cols
-    ref = O.onebit_linear(c.X[rows], c.W_sign[cols], c.a[cols], c.b)
-    err = O.max_normalised_error(Yh[np.ix_(rows, cols)], ref, O.onebit_error_scale(c.X[rows], c.a[cols], c.b))
+    Yref, S = t_linear(torch, X, Spm1, a0, b0)
+    err = t_err(torch, Y, Yref, S)
+    del Spm1, Yref, S
     launches = [(lambda W=W, a=a, b=b: B.linear(X, W, a, b, out=Y)) for (W, a, b) in copies]
     return c, launches, err, R
 
 
-def dbf_setup(torch, B, WL, O, rotate_bytes):
-    import numpy as np
+def dbf_setup(torch, B, WL, rotate_bytes):
     c = WL.workload(5)
     dev = torch.device("cuda")
     X = torch.from_numpy(c.X).to(torch.float32).to(torch.bfloat16).to(dev)
     sc = [torch.from_numpy(v).to(torch.float32).to(torch.float16).to(dev) for v in (c.b, c.m, c.a)]
-    S2 = B.pack_signs(torch.from_numpy(c.S2).to(dev))
-    S1 = B.pack_signs(torch.from_numpy(c.S1).to(dev))
+    S2d, S1d = torch.from_numpy(c.S2).to(dev), torch.from_numpy(c.S1).to(dev)
+    S2 = B.pack_signs(S2d)
+    S1 = B.pack_signs(S1d)
     per_copy = (S2.numel() + S1.numel()) * 4 + sum(t.numel() * 2 for t in sc)
     R = max(1, -(-rotate_bytes // per_copy))
     copies = [(S2, S1, *sc)] + [(S2.clone(), S1.clone(), *[t.clone() for t in sc]) for _ in range(R - 1)]
     Y = torch.empty((c.M, c.N), dtype=torch.float32, device=dev)
     ws = torch.empty((c.M, c.Kmid), dtype=torch.float32, device=dev)
     B.dbf_linear(X, S2, S1, *sc, workspace=ws, out=Y)
-    torch.cuda.synchronize()
-    err = O.max_normalised_error(Y.cpu().numpy().astype(np.float64),
-                                 O.dbf_linear(c.X, c.S1, c.S2, c.a, c.m, c.b),
-                                 O.dbf_error_scale(c.X, c.b, c.m, c.a))
+    err = t_err(torch, Y, *t_dbf(torch, X, S2d, S1d, *sc))
     launches = [(lambda s2=s2, s1=s1, b=b, m=m, a=a: B.dbf_linear(X, s2, s1, b, m, a, workspace=ws, out=Y))
                 for (s2, s1, b, m, a) in copies]
     return c, launches, err, R
 
 
-def dbf_prefill_setup(torch, B, WL, O, M=512, K=4096, Kmid=3072, N=4096, copies=8):
-    """DBF prefill (two MFMA GEMMs with the m mid-scale), sampled-row parity."""
-    import numpy as np
+def dbf_prefill_setup(torch, B, WL, M=512, K=4096, Kmid=3072, N=4096, copies=8):
+    """DBF prefill (two MFMA GEMMs with the m mid-scale)."""
     c = WL.dbf_case(M, K, Kmid, N, seed=Kmid, name=f"dbf-prefill-{M}x{K}-{Kmid}-{N}")
     dev = torch.device("cuda")
     X = torch.from_numpy(c.X).to(torch.float32).to(torch.bfloat16).to(dev)
     sc = [torch.from_numpy(v).to(torch.float32).to(torch.float16).to(dev) for v in (c.b, c.m, c.a)]
-    S2 = B.pack_signs(torch.from_numpy(c.S2).to(dev))
-    S1 = B.pack_signs(torch.from_numpy(c.S1).to(dev))
+    S2d, S1d = torch.from_numpy(c.S2).to(dev), torch.from_numpy(c.S1).to(dev)
+    S2 = B.pack_signs(S2d)
+    S1 = B.pack_signs(S1d)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((M, Kmid), dtype=torch.float32, device=dev)
     B.dbf_linear(X, S2, S1, *sc, workspace=ws, out=Y)
-    torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.random.default_rng(1).choice(M, 16, replace=False), [0, M - 1]]))
-    err = O.max_normalised_error(Y.float().cpu().numpy().astype(np.float64)[rows],
-                                 O.dbf_linear(c.X[rows], c.S1, c.S2, c.a, c.m, c.b),
-                                 O.dbf_error_scale(c.X[rows], c.b, c.m, c.a))
+    err = t_err(torch, Y, *t_dbf(torch, X, S2d, S1d, *sc))
     reps = [(S2, S1)] + [(S2.clone(), S1.clone()) for _ in range(copies - 1)]
     launches = [(lambda s2=s2, s1=s1: B.dbf_linear(X, s2, s1, *sc, workspace=ws, out=Y)) for (s2, s1) in reps]
     return c, launches, err, copies
 
 
-def backward_setup(torch, B, WL, O, M, K, N, copies):
-    """Backward of the layer (dX, da, db) on synthetic dY; parity on sampled rows
-    of dX and on da, db (full, the oracle is a dense fp64 product)."""
+def backward_setup(torch, B, WL, M, K, N, copies):
+    """Backward of the layer (dX, da, db) on synthetic dY; guard: max error of
+    each output relative to that output's largest magnitude."""
     import numpy as np
     rng = np.random.default_rng(M + K + N)
     X = WL.round_to(rng.standard_normal((M, K)), "bf16")
@@ -190,24 +209,27 @@ def backward_setup(torch, B, WL, O, M, K, N, copies):
     dev = torch.device("cuda")
     t = lambda v, dt: torch.from_numpy(v).to(torch.float32).to(dt).to(dev)
     Xd, dYd, ad, bd = t(X, torch.bfloat16), t(dY, torch.bfloat16), t(a, torch.float16), t(b, torch.float16)
-    W = B.pack_signs(torch.from_numpy(S).to(dev))
+    Sd = torch.from_numpy(S).to(dev)
+    W = B.pack_signs(Sd)
     Wt = B.transpose_signs(W, N, K)
     ws = torch.empty(M * (N + K), dtype=torch.float32, device=dev)
     dX, da, db, _ = B.linear_backward(dYd, Xd, W, Wt, ad, bd, workspace=ws)
-    torch.cuda.synchronize()
-    rdX, rda, rdb = O.onebit_backward(X, S, a, b, dY)
-    sdx, sda, sdb = O.backward_error_scales(X, a, b, dY)
-    err = max(O.max_normalised_error(dX.float().cpu().numpy().astype(np.float64), rdX, sdx),
-              O.max_normalised_error(da.cpu().numpy().astype(np.float64), rda, sda),
-              O.max_normalised_error(db.cpu().numpy().astype(np.float64), rdb, sdb))
+    Sf = Sd.float()
+    T = (Xd.float() * bd.float()) @ Sf.t()
+    U = (dYd.float() * ad.float()) @ Sf
+    refs = (U * bd.float(), (dYd.float() * T).sum(0), (Xd.float() * U).sum(0))
+    err = max(float((g.double() - r.double()).abs().max() / r.double().abs().max())
+              for g, r in zip((dX, da, db), refs))
     reps = [(W, Wt)] + [(W.clone(), Wt.clone()) for _ in range(copies - 1)]
     launches = [(lambda w=w, wt=wt: B.linear_backward(dYd, Xd, w, wt, ad, bd, workspace=ws)) for (w, wt) in reps]
     return launches, err
 
 
-def cpu_baseline(WL, O, budget_s: float = 12.0):
-    """Time the fp64 oracle on workload 2 (the headline) for a bounded sample."""
+def cpu_baseline(WL, budget_s: float = 12.0):
+    """Time the fp64 oracle on workload 2 (the headline) for a bounded sample.
+    The only place bench.py uses the oracle."""
     import numpy as np
+    import oracle as O
     c = WL.workload(2)
     try:
         from threadpoolctl import threadpool_info
@@ -254,7 +276,6 @@ def main():
     import numpy as np
     import torch
 
-    import oracle as O
     from bit_weight_linear_amd import workloads as WL
 
     B = load_binding()
@@ -262,9 +283,10 @@ def main():
     rot = int(args.rotate_gib * (1 << 30))
 
     # ---------------- headline: workload 2, M = 1 decode GEMV
-    c, launches, err, R = onebit_setup(torch, B, WL, O, 2, rot)
-    log(f"[bench] {c.name}: parity max normalised error {err:.3e}; {R} weight copies")
-    assert err <= 1e-5, "parity failed on the timed configuration"
+    torch.backends.cuda.matmul.allow_tf32 = False    # the guards compare against plain fp32 products
+    c, launches, err, R = onebit_setup(torch, B, WL, 2, rot)
+    log(f"[bench] {c.name}: guard vs fp32 torch, max normalised error {err:.3e}; {R} weight copies")
+    assert err <= 1e-4, "the timed configuration disagrees with the fp32 guard"
     t = Timed(torch, launches)
     ms_step, ms_launch = t.run(args.warmup, args.steps)
     wbytes = c.N * c.K // 8
@@ -294,7 +316,8 @@ def main():
                      "traffic": traffic},
         "us_per_launch": round(ms_launch * 1e3, 4),
         "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
-        "parity_max_normalised_error": float(f"{err:.3e}"),
+        "check_vs_torch_fp32": float(f"{err:.3e}"),
+        "parity": "against the fp64 oracle in tests/test_gpu_parity.py (test_workload2_decode_gemv, full size)",
     }
     del launches, t
     torch.cuda.empty_cache()
@@ -302,26 +325,23 @@ def main():
     # ---------------- secondary workloads
     if not args.no_secondary:
         sec = {}
-        rng = np.random.default_rng(0)
         # workload 4: prefill GEMM, M = 2048
-        rows = np.unique(np.concatenate([rng.choice(2048, 32, replace=False), [0, 2047]]))
-        cols = np.unique(np.concatenate([rng.choice(14336, 96, replace=False), [0, 14335]]))
-        c4, l4, e4, R4 = onebit_setup(torch, B, WL, O, 4, min(rot, 64 << 20), rows, cols)
-        assert e4 <= 8e-3, "parity failed on workload 4"
+        c4, l4, e4, R4 = onebit_setup(torch, B, WL, 4, min(rot, 64 << 20))
+        assert e4 <= 1e-2, "workload 4 disagrees with the fp32 guard"
         t4 = Timed(torch, l4)
         ms4_step, ms4 = t4.run(2, max(3, args.steps // 4))
         flops = 2.0 * c4.M * c4.N * c4.K
         tflops = flops / (ms4 * 1e-3) / 1e12
         sec[c4.name] = {"us_per_launch": round(ms4 * 1e3, 2), "TOPS": round(tflops, 2),
                         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
-                        "parity_max_normalised_error_sampled": float(f"{e4:.3e}"), "copies": R4}
+                        "check_vs_torch_fp32": float(f"{e4:.3e}"), "copies": R4}
         log(f"[bench] {c4.name}: {ms4 * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
         del l4, t4
         torch.cuda.empty_cache()
         # workloads 1, 3: decode kernel
         for i in (3, 1):
-            ci, li, ei, Ri = onebit_setup(torch, B, WL, O, i, rot if i == 3 else (64 << 20))
-            assert ei <= 1e-5, f"parity failed on workload {i}"
+            ci, li, ei, Ri = onebit_setup(torch, B, WL, i, rot if i == 3 else (64 << 20))
+            assert ei <= 1e-4, f"workload {i} disagrees with the fp32 guard"
             ti = Timed(torch, li)
             _, msi = ti.run(args.warmup, args.steps)
             wb = ci.N * ci.K / 8
@@ -332,12 +352,12 @@ def main():
                             "algorithmic_bytes": int(ab), "ideal_us_hbm": round(ab / HBM_PEAK_GBS / 1e3, 4),
                             "hbm_frac": round(ab / (msi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                             "bound": "latency (launch and one HBM round trip; the HBM time is a fraction of it)",
-                            "parity_max_normalised_error": float(f"{ei:.3e}"), "copies": Ri}
+                            "check_vs_torch_fp32": float(f"{ei:.3e}"), "copies": Ri}
             log(f"[bench] {ci.name}: {msi * 1e3:.2f} us")
             del li, ti
         # workload 5: DBF
-        c5, l5, e5, R5 = dbf_setup(torch, B, WL, O, rot)
-        assert e5 <= 1e-5, "parity failed on workload 5"
+        c5, l5, e5, R5 = dbf_setup(torch, B, WL, rot)
+        assert e5 <= 1e-4, "workload 5 disagrees with the fp32 guard"
         t5 = Timed(torch, l5)
         _, ms5 = t5.run(args.warmup, args.steps)
         wb5 = c5.Kmid * (c5.K + c5.N) / 8
@@ -346,30 +366,30 @@ def main():
                         "algorithmic_bytes": int(ab5), "ideal_us_hbm": round(ab5 / HBM_PEAK_GBS / 1e3, 4),
                         "hbm_frac": round(ab5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "bound": "latency (two stages, four launches)",
-                        "parity_max_normalised_error": float(f"{e5:.3e}"), "copies": R5,
+                        "check_vs_torch_fp32": float(f"{e5:.3e}"), "copies": R5,
                         "stages_per_call": 2}
         log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
         del l5, t5
         # DBF prefill (M = 512, Kmid = 3072: 1.5 sign bits per weight)
-        c6, l6, e6, R6 = dbf_prefill_setup(torch, B, WL, O)
-        assert e6 <= 1.2e-2, "parity failed on the DBF prefill"
+        c6, l6, e6, R6 = dbf_prefill_setup(torch, B, WL)
+        assert e6 <= 1.5e-2, "the DBF prefill disagrees with the fp32 guard"
         t6 = Timed(torch, l6)
         _, ms6 = t6.run(2, max(3, args.steps // 4))
         fl6 = 2.0 * c6.X.shape[0] * c6.S2.shape[0] * (c6.S2.shape[1] + c6.S1.shape[0])
         tf6 = fl6 / (ms6 * 1e-3) / 1e12
         sec[c6.name] = {"us_per_call": round(ms6 * 1e3, 2), "TOPS": round(tf6, 2),
                         "mfma_frac": round(tf6 / BF16_PEAK_TFLOPS, 4),
-                        "parity_max_normalised_error_sampled": float(f"{e6:.3e}"), "copies": R6}
+                        "check_vs_torch_fp32": float(f"{e6:.3e}"), "copies": R6}
         log(f"[bench] {c6.name}: {ms6 * 1e3:.1f} us per call, {tf6:.1f} TFLOP/s")
         del l6, t6
         # backward of the layer at the batched-decode shape (two sign contractions + reductions)
-        l7, e7 = backward_setup(torch, B, WL, O, 16, 4096, 4096, copies=64)
-        assert e7 <= 1e-5, "parity failed on the backward"
+        l7, e7 = backward_setup(torch, B, WL, 16, 4096, 4096, copies=64)
+        assert e7 <= 1e-4, "the backward disagrees with the fp32 guard"
         t7 = Timed(torch, l7)
         _, ms7 = t7.run(args.warmup, args.steps)
         sec["backward-16x4096x4096"] = {"us_per_call": round(ms7 * 1e3, 3),
                                         "weight_GBps": round(2 * 4096 * 4096 / 8 / (ms7 * 1e-3) / 1e9, 1),
-                                        "parity_max_normalised_error": float(f"{e7:.3e}"), "copies": 64,
+                                        "check_vs_torch_fp32": float(f"{e7:.3e}"), "copies": 64,
                                         "note": "weight bytes counted twice: W and its transposed packing"}
         log(f"[bench] backward-16x4096x4096: {ms7 * 1e3:.2f} us per call")
         del l7, t7
@@ -377,7 +397,8 @@ def main():
         rng8 = np.random.default_rng(8)
         Wd = torch.from_numpy(WL.round_to(rng8.standard_normal((11008, 4096)) * 0.02, "f16")).to(torch.float16).cuda()
         P8, a8, b8 = B.svid(Wd, iters=32)
-        torch.cuda.synchronize()
+        assert bool(torch.isfinite(a8.float()).all() and (a8.float() > 0).all() and (b8.float() > 0).all()), \
+            "SVID scales not finite and positive"
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
         for _ in range(3):
@@ -399,43 +420,40 @@ def main():
         be9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.1, "f16")).to(torch.float16).cuda()
         Z9 = torch.empty((M9, N9), dtype=torch.bfloat16, device="cuda")
         B.layernorm(Y9[0], 1e-5, g9, be9, out=Z9)
-        torch.cuda.synchronize()
-        r9 = np.array([0, 1, 777, M9 - 1])
-        y9h = Y9[0][torch.from_numpy(r9).cuda()].cpu().numpy().astype(np.float64)
-        z9ref = O.layernorm_rows(y9h, 1e-5, g9.float().cpu().numpy().astype(np.float64),
-                                 be9.float().cpu().numpy().astype(np.float64))
-        e9 = float(np.max(np.abs(Z9[torch.from_numpy(r9).cuda()].float().cpu().numpy() - z9ref)
-                          / (np.abs(z9ref) + 1.0)))
-        assert e9 <= 2.0 ** -7, "parity failed on the LayerNorm"
+        z9ref = torch.nn.functional.layer_norm(Y9[0], (N9,), g9.float(), be9.float(), 1e-5)
+        e9 = float(((Z9.float() - z9ref).abs() / (z9ref.abs() + 1.0)).max())
+        del z9ref
+        assert e9 <= 2.0 ** -7, "the LayerNorm disagrees with the fp32 guard"
         t9 = Timed(torch, [(lambda y=y: B.layernorm(y, 1e-5, g9, be9, out=Z9)) for y in Y9])
         _, ms9 = t9.run(args.warmup, args.steps)
         by9 = M9 * N9 * (4 + 2) + 2 * N9 * 2
         sec["layernorm-2048x14336-f32-bf16"] = {
             "us_per_launch": round(ms9 * 1e3, 3), "GBps": round(by9 / (ms9 * 1e-3) / 1e9, 1),
             "hbm_frac": round(by9 / (ms9 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
-            "algorithmic_bytes": by9, "parity_max_rel_error_sampled": float(f"{e9:.3e}")}
+            "algorithmic_bytes": by9, "check_vs_torch_fp32": float(f"{e9:.3e}")}
         log(f"[bench] layernorm-2048x14336: {ms9 * 1e3:.2f} us, {by9 / (ms9 * 1e-3) / 1e9:.0f} GB/s")
         del t9, Y9, Z9
         # the decode layer followed by LayerNorm in one call (headline shape)
         c10 = WL.workload(2)
         X10 = torch.from_numpy(c10.X).to(torch.float32).to(torch.bfloat16).cuda()
-        W10 = B.pack_signs(torch.from_numpy(c10.W_sign).cuda())
+        S10 = torch.from_numpy(c10.W_sign).cuda()
+        W10 = B.pack_signs(S10)
         a10 = torch.from_numpy(c10.a).to(torch.float32).to(torch.float16).cuda()
         b10 = torch.from_numpy(c10.b).to(torch.float32).to(torch.float16).cuda()
         reps10 = [(W10, a10, b10)] + [(W10.clone(), a10.clone(), b10.clone()) for _ in range(R - 1)]
         ws10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
         Z10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
         B.linear_layernorm(X10, W10, a10, b10, 1e-5, workspace=ws10, out=Z10)
-        torch.cuda.synchronize()
-        y10 = O.onebit_linear(c10.X, c10.W_sign, c10.a, c10.b)
-        e10 = float(np.max(np.abs(Z10.cpu().numpy().astype(np.float64) - O.layernorm_rows(y10, 1e-5))))
-        assert e10 <= 1e-3, "parity failed on the layer + LayerNorm"
+        y10, _ = t_linear(torch, X10, S10, a10, b10)
+        e10 = float((Z10 - torch.nn.functional.layer_norm(y10, (c10.N,), None, None, 1e-5)).abs().max())
+        del S10, y10
+        assert e10 <= 1e-3, "the layer + LayerNorm disagrees with the fp32 guard"
         t10 = Timed(torch, [(lambda w=w, a=a, b=b: B.linear_layernorm(X10, w, a, b, 1e-5, workspace=ws10, out=Z10))
                             for (w, a, b) in reps10])
         _, ms10 = t10.run(args.warmup, args.steps)
         sec[f"linear-layernorm-{c10.name}"] = {"us_per_call": round(ms10 * 1e3, 3),
                                                "weight_GBps": round(wbytes / (ms10 * 1e-3) / 1e9, 1),
-                                               "max_abs_error_vs_oracle": float(f"{e10:.3e}"), "copies": R,
+                                               "check_vs_torch_fp32_abs": float(f"{e10:.3e}"), "copies": R,
                                                "launches_per_call": 2}
         log(f"[bench] linear-layernorm-{c10.name}: {ms10 * 1e3:.2f} us per call")
         del t10, reps10
@@ -452,7 +470,7 @@ def main():
         del src, dst
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(WL, O)
+        out["cpu_baseline"] = cpu_baseline(WL)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']} GB/s")
     print(json.dumps(out), flush=True)
 
