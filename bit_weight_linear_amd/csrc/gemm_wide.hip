@@ -55,6 +55,7 @@
 //    and the reduction reading them back; counting that traffic, more
 //    slices of fewer stages stop paying at about 8.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "obl_common.hpp"
@@ -68,11 +69,8 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GW_THREADS = 256;
 constexpr int GW_BM = 128;        // workgroup rows
-constexpr int GW_BN = 448;        // workgroup columns
 constexpr int GW_WM = 64;         // wave rows
-constexpr int GW_WN = 224;        // wave columns
 constexpr int GW_FM = GW_WM / 32; // 2 activation fragments
-constexpr int GW_FN = GW_WN / 32; // 7 sign fragments
 constexpr int GW_KT = 128;        // k per stage
 constexpr int GW_S = GW_KT / 16;  // MFMA k-steps per stage
 
@@ -109,26 +107,38 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_b
 }
 
 constexpr int GW_XDMA = GW_BM * (GW_KT / 8) / 64 / 4;    // activation DMAs per wave per stage (8)
-constexpr int GW_WCOLS = 512;                             // sign columns staged (>= GW_BN, 2 DMAs per wave)
 constexpr int GW_BTAB_BATCH = 8 * GW_THREADS;             // bf16(b) pairs per table-fill batch
-static_assert(GW_BN <= 2 * GW_THREADS, "two output scales per thread");
+constexpr double GW_EFF4 = 1.08;                          // per-column cost of the 256-wide tile vs the 448-wide
+
+// Column tiling, by sign fragments (32 columns) per wave: FN = 7 gives the
+// 64 x 224 wave tile and 128 x 448 workgroup tile, FN = 4 a 64 x 128 wave
+// tile and 128 x 256 workgroup tile.  Sign columns are staged in whole
+// 256-column DMA rounds (one 16-byte DMA per lane per round).
+template <int FN> struct GwTile {
+  static constexpr int WN = 32 * FN;                      // wave columns
+  static constexpr int BN = 2 * WN;                       // workgroup columns
+  static constexpr int WCOLS = (BN + 255) / 256 * 256;    // sign columns staged
+  static constexpr int WDMA = WCOLS / 256;                // sign DMAs per wave per stage
+  static_assert(BN <= 2 * GW_THREADS, "two output scales per thread");
+};
 
 // Entries of the bf16(b) pair table: K / 2 rounded up to whole fill batches.
 inline int64_t gw_btab_entries(int64_t K) {
   return (K / 2 + GW_BTAB_BATCH - 1) / GW_BTAB_BATCH * GW_BTAB_BATCH;
 }
-constexpr int GW_WDMA = GW_WCOLS / 64 / 4;                // sign DMAs per wave per stage (2)
 
 // SPLIT: block b takes tile b / nsplit and the 128-k stages
 // [s·per, min((s + 1)·per, K/128)) of slice s = b % nsplit, and writes its raw
 // fp32 sums (no output scale) to part[s][M][N]; gemm_split_reduce_kernel adds
 // the slices in order.
-template <typename ST, typename YT, bool PRE, bool SPLIT>
+template <typename ST, typename YT, bool PRE, bool SPLIT, int FN>
 __global__ __launch_bounds__(GW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W,
                       int64_t N, const ST* __restrict__ pre, const ST* __restrict__ post,
                       YT* __restrict__ Y, bf16_t* __restrict__ Y2, int mt, int nt, int xcd_groups,
                       int nsplit, int per, float* __restrict__ part) {
+  constexpr int GW_WN = GwTile<FN>::WN, GW_BN = GwTile<FN>::BN, GW_FN = FN;
+  constexpr int GW_WCOLS = GwTile<FN>::WCOLS, GW_WDMA = GwTile<FN>::WDMA;
   // Three stage buffers as distinct LDS objects: the K loop is unrolled by
   // three so every access names its buffer, and the compiler can tell a DMA
   // into one buffer from reads of another.
@@ -430,10 +440,11 @@ int split_count(int64_t tiles, int64_t nk, int num_cus) {
   return (int)std::max<int64_t>(s, 1);
 }
 
-template <typename ST, typename YT, bool PRE>
-hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
+template <typename ST, typename YT, bool PRE, int FN>
+hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
+  constexpr int BN = GwTile<FN>::BN;
   const int64_t mt = (a.M + GW_BM - 1) / GW_BM;
-  const int64_t nt = (a.N + GW_BN - 1) / GW_BN;
+  const int64_t nt = (a.N + BN - 1) / BN;
   const int64_t tiles = mt * nt;
   const int64_t nk = a.K / GW_KT;
   const size_t lds = (PRE ? gw_btab_entries(a.K) : 0) * sizeof(uint32_t);
@@ -444,7 +455,7 @@ hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
     float* part = nullptr;
     hipError_t e = split_reserve(dev.device, (size_t)nsplit * (size_t)(a.M * a.N), &part);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_wide_kernel<ST, float, PRE, true>), dim3((unsigned)(tiles * nsplit)),
+    hipLaunchKernelGGL((gemm_wide_kernel<ST, float, PRE, true, FN>), dim3((unsigned)(tiles * nsplit)),
                        dim3(GW_THREADS), lds, a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                        static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post), nullptr, nullptr, (int)mt,
                        (int)nt, 1, nsplit, per, part);
@@ -460,11 +471,39 @@ hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
     return hipGetLastError();
   }
   const int xcd = (tiles % 8 == 0) ? 8 : 1;
-  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE, false>), dim3((unsigned)tiles), dim3(GW_THREADS), lds,
+  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE, false, FN>), dim3((unsigned)tiles), dim3(GW_THREADS), lds,
                      a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                      static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post),
                      static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.Y2), (int)mt, (int)nt, xcd, 1, 0, nullptr);
   return hipGetLastError();
+}
+
+// Column-tile width.  A grid that splits K with the 256-wide tile takes it
+// (more tiles, fewer slices: less partial-sum traffic; measured at M = 512:
+// 512x4096x3072 30.5 vs 38.4 us).  Otherwise the estimated time is the number
+// of rounds of one workgroup per CU times the tile width, with `GW_EFF4` the
+// relative per-column cost of the narrow tile.  Measured at M = 2048, K = 4096:
+// N = 14336 keeps 448 (217 vs 245 us), N = 11008 and N = 4096 take 256
+// (182 vs 198 us, 67 vs 96 us).  OBL_GEMM=w4 / w7 forces a width (tests).
+int64_t rounds(int64_t M, int64_t N, int bn, int cus) {
+  const int64_t tiles = ((M + GW_BM - 1) / GW_BM) * ((N + bn - 1) / bn);
+  return (tiles + cus - 1) / cus;
+}
+
+int pick_fn(int64_t M, int64_t N, int cus) {
+  const char* e = std::getenv("OBL_GEMM");
+  if (e && e[0] == 'w' && e[1] == '4') return 4;
+  if (e && e[0] == 'w' && e[1] == '7') return 7;
+  const int64_t tiles4 = ((M + GW_BM - 1) / GW_BM) * ((N + GwTile<4>::BN - 1) / GwTile<4>::BN);
+  if (tiles4 * 2 <= cus) return 4;
+  const double u4 = (double)rounds(M, N, GwTile<4>::BN, cus) * GwTile<4>::BN * GW_EFF4;
+  const double u7 = (double)rounds(M, N, GwTile<7>::BN, cus) * GwTile<7>::BN;
+  return u4 < u7 ? 4 : 7;
+}
+
+template <typename ST, typename YT, bool PRE>
+hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
+  return pick_fn(a.M, a.N, dev.num_cus) == 4 ? launch_fn<ST, YT, PRE, 4>(a, dev) : launch_fn<ST, YT, PRE, 7>(a, dev);
 }
 
 template <typename ST>
@@ -578,7 +617,7 @@ bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const voi
   // out-of-range sentinel), and the grid in an int.
   const int64_t lim = (int64_t)0xFFFFF000u;
   if (a.M * a.K * 2 > lim || a.N * (a.K / 32) * 4 > lim) return false;
-  const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GW_BN - 1) / GW_BN);
+  const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GwTile<4>::BN - 1) / GwTile<4>::BN);
   if (tiles > 0x7fffffff) return false;
   // LDS: the bf16(b) table (2K bytes rounded up to 8 KiB batches, dynamic)
   // next to ~124 KiB of static stage buffers.

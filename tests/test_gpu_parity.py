@@ -100,10 +100,12 @@ GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("bf16", "f32", 
 
 @pytest.mark.parametrize("M,K,N", GEMM_CASES)
 @pytest.mark.parametrize("dts", GEMM_DTYPES, ids=lambda d: "-".join(d))
-@pytest.mark.parametrize("impl", ["auto", "v2", "v1"])
+@pytest.mark.parametrize("impl", ["auto", "w7", "w4", "v2", "v1"])
 def test_gemm_path(M, K, N, dts, impl, monkeypatch):
-    """impl=auto picks the register-staged 32x32 kernel where it applies (bf16 x,
-    K % 128 == 0), v2 the LDS-staged kernel, v1 the 8-wave kernel everywhere."""
+    """impl=auto picks the main 32x32 kernel where it applies (K % 128 == 0;
+    fp32 or misaligned x through the prescale pass) and its tile width; w7 / w4
+    force the 448- / 256-column tile, v2 the LDS-staged 16x16 kernel, v1 the
+    8-wave kernel."""
     if impl != "auto":
         monkeypatch.setenv("OBL_GEMM", impl)
     G.say(f"gemm[{impl}] M={M} K={K} N={N} {dts}")
@@ -169,6 +171,25 @@ def test_workload4_prefill_sampled():
     G.say(f"  sampled max normalised error {r:.3e}")
     assert r <= G.TOL_GEMM
     assert np.isfinite(Y).all()
+
+
+@pytest.mark.parametrize("impl", ["auto", "w7"])
+def test_prefill_down_projection_sampled(impl, monkeypatch):
+    """2048 x 11008 -> 4096 (a Llama-2-7B MLP down projection): the tile-width
+    choice takes 256 columns here (auto); w7 checks the 448-column tile with a
+    partial last column tile.  Sampled outputs against the oracle."""
+    if impl != "auto":
+        monkeypatch.setenv("OBL_GEMM", impl)
+    c = WL.onebit_case(2048, 11008, 4096, "bf16", "f16", "bf16", seed=21)
+    G.say(f"{c.name} [{impl}]")
+    Y = G.run_onebit(c, "gemm")
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.choice(c.M, 32, replace=False), [0, c.M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(c.N, 96, replace=False), [0, 255, 256, 447, 448, c.N - 1]]))
+    Yr = O.onebit_linear(c.X[rows], c.W_sign[cols], c.a[cols], c.b)
+    r = O.max_normalised_error(Y[np.ix_(rows, cols)], Yr, O.onebit_error_scale(c.X[rows], c.a[cols], c.b))
+    G.say(f"  sampled max normalised error {r:.3e}")
+    assert r <= G.TOL_GEMM and np.isfinite(Y).all()
 
 
 def test_workload5_dbf():
