@@ -18,9 +18,13 @@
 //       bf16 terms hi + mid + lo (24 significant bits), B = ±1, 3 MFMAs.
 // The sign operand is expanded in registers from the packed words.
 //
-// Work split: block = 4 waves x 16 columns (64 output columns) x one K-slice
-// of 512 k, so each block reads only its slice of X (a whole-K block would pull
-// all of X through every CU's L1, which measured slower).  With one slice the
+// Two kernels share the contraction below.  The whole-K kernel (further down)
+// serves bf16 x with fp16 b and aligned operands in one launch: a workgroup
+// owns a column block over all of K and adds its waves' slice sums in LDS.
+// The split kernel serves everything else (fp32 x or b, misaligned operands).
+//
+// Split kernel work split: block = 4 waves x 16 columns (64 output columns) x
+// one K-slice of 512 k, so each block reads only its slice of X.  With one slice the
 // block applies the post scale and writes Y; otherwise slices write fp32
 // partial sums to scratch and a second small kernel adds them in slice order
 // (the kernel boundary orders the memory traffic; no fences, no atomics), so
@@ -46,6 +50,7 @@
 // The contraction takes four steps at a time: all LDS reads of the four are
 // issued before the first MFMA and each step owns its accumulators.
 #include <cstdlib>
+#include <cstring>
 
 #include "obl_common.hpp"
 #include "obl_internal.hpp"
@@ -354,6 +359,243 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   Store<YT>::put(&Y[e], acc * s);
 }
 
+// ---------------------------------------------------------------------------
+// Whole-K variant (bf16 x and fp16 b: mode B2; 16-byte aligned X and W, K %
+// 128 == 0).  A workgroup of 8 waves owns 16·CPW output columns over all of K;
+// wave w takes the 512-k slices w, w + 8, ... of them.  Per slice the wave
+// stages its M rows of X in its own LDS region (one 1 KiB DMA per row, the
+// same swizzle as above), loads its columns' 16 sign words per column straight
+// into registers (the four lanes of a column load the same words), builds the
+// slice's (b_hi, b_lo) pair tables, and contracts the slice as above; no
+// workgroup barrier is needed until the end, where the eight per-wave sums of
+// each output are added in wave order through LDS and the post scale applied.
+// One launch, and no partial sums through HBM: the split-K kernel needs a
+// second launch for its slice reduction, which must wait for the first.  The
+// price is that every workgroup reads all of X (M·K·2 bytes through its CU).
+// With one column group per wave and K <= 4096 (one slice per wave) the sums
+// are added in exactly the split kernel's order: both give bitwise the same
+// results.
+constexpr int WK_WAVES = 8;
+constexpr int WK_THREADS = 64 * WK_WAVES;
+
+// LDS of one wave (16-byte units): M rows x 64 X chunks, then 64 b_hi and 64
+// b_lo pair quads.  After the contraction the area holds the reduction table.
+__host__ __device__ inline size_t wk_wave_units(int64_t M) { return (size_t)M * 64 + 128; }
+inline size_t wk_lds_bytes(int64_t M, int cpw) {
+  const size_t stage = (size_t)WK_WAVES * wk_wave_units(M) * 16;
+  const size_t red = (size_t)WK_WAVES * 16 * (16 * cpw + 1) * sizeof(float);
+  return stage > red ? stage : red;
+}
+
+template <int MODE, typename ST, typename YT, int CPW>
+__global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
+    const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
+    const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y) {
+  static_assert(MODE == MODE_B1 || MODE == MODE_B2, "bf16 activations only");
+  constexpr int NA = MODE == MODE_B1 ? 1 : 2;
+  constexpr int NC = 16 * CPW;                                    // columns per workgroup
+  constexpr int RS = NC + 1;                                      // reduction table row stride (floats)
+  constexpr int NOUT = (16 * NC + WK_THREADS - 1) / WK_THREADS;   // final outputs per thread
+  extern __shared__ u32x4 wk_lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t kw = K >> 5;
+  const int nslices = (int)((kw + DEC_STEPS - 1) / DEC_STEPS);
+  const int64_t n0 = (int64_t)blockIdx.x * NC;
+  u32x4* xw = wk_lds + (size_t)wave * wk_wave_units(M);          // this wave's X chunks
+  uint32_t* mw = reinterpret_cast<uint32_t*>(xw + (size_t)M * 64);   // b_hi pairs [256], b_lo pairs [256]
+
+  // Output scales of this thread's final outputs (o = tid + WK_THREADS r is
+  // row o / NC, column o % NC), issued before the streams.
+  float post_o[NOUT];
+#pragma unroll
+  for (int r = 0; r < NOUT; ++r)
+    post_o[r] = scale_or_one(post, min(n0 + (tid + WK_THREADS * r) % NC, N - 1), W);   // W: >= 4N bytes
+
+  u16x2 sh[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = 8 * (g & 1) + 2 * r;
+    sh[r] = u16x2{(unsigned short)(15 - p), (unsigned short)(14 - p)};
+  }
+  const int h = g >> 1;
+  const bool mrow = j < M;
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const int xrow = (mrow ? j : 0) * 64;
+  const int swz = j & 15;
+
+  // Accumulator sets: step t adds into set t % AU.  With one column group
+  // each of four consecutive steps owns a set (the split kernel's order);
+  // with more, the column groups already give the MFMAs enough independent
+  // chains and fewer sets keep the registers within two waves per SIMD.
+  constexpr int AU = CPW == 1 ? 4 : (CPW == 2 ? 2 : 1);
+  f32x4 acc[AU][CPW][NA];
+#pragma unroll
+  for (int u = 0; u < AU; ++u)
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int a = 0; a < NA; ++a) acc[u][c][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = wave; s < nslices; s += WK_WAVES) {
+    const int64_t step0 = (int64_t)s * DEC_STEPS;
+    const int64_t k0 = step0 * 32;
+    const int nsteps = (int)min((int64_t)DEC_STEPS, kw - step0);   // a multiple of 4
+    // X: row r by one DMA, lane l -> slot l = chunk l ^ (r % 16); chunks past
+    // K re-read chunk 0 of the slice (never used).
+    for (int r = 0; r < M; ++r) {
+      int64_t ke = k0 + 8 * (int64_t)(lane ^ (r & 15));
+      if (ke >= K) ke = k0;
+      load_lds16(X + (int64_t)r * K + ke, xw + r * 64);
+    }
+    // Sign words: all 16 of the slice for each of this lane's columns; quads
+    // past the end re-read quad 0 (masked below).
+    u32x4 wq[CPW][4];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint32_t* src = W + min(n0 + 16 * c + j, N - 1) * kw + step0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wq[c][q] = *reinterpret_cast<const u32x4*>(src + (4 * q < nsteps ? 4 * q : 0));
+    }
+    // Mode B2: b pairs (lane + 64 i) of the slice.
+    float bp[4][2];
+    if constexpr (MODE == MODE_B2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t k = k0 + 2 * (lane + 64 * i);
+        const int64_t kc = k < K ? k : 0;
+        bp[i][0] = to_f32(pre[kc]);
+        bp[i][1] = to_f32(pre[kc + 1]);
+        if (k >= K) bp[i][0] = bp[i][1] = 0.f;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the slice is in LDS and registers
+    if constexpr (MODE == MODE_B2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float h0 = bf16_round(bp[i][0]), h1 = bf16_round(bp[i][1]);
+        mw[lane + 64 * i] = pack_bf16_pair(h0, h1);
+        mw[256 + lane + 64 * i] = pack_bf16_pair(bp[i][0] - h0, bp[i][1] - h1);   // exact (fp16 residual)
+      }
+    }
+    // Only this wave writes and reads its region: order its LDS writes before
+    // its reads, no workgroup barrier.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+    for (int t = 0; t < DEC_STEPS; t += 4) {
+      u32x4 xf[4], mh[4], ml[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kb = 32 * (t + u) + 8 * g;
+        xf[u] = xw[xrow + ((kb / 8) ^ swz)];
+        if constexpr (MODE == MODE_B2) {
+          mh[u] = *reinterpret_cast<const u32x4*>(mw + kb / 2);
+          ml[u] = *reinterpret_cast<const u32x4*>(mw + 256 + kb / 2);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 a = (mrow && (t + u < nsteps)) ? xf[u] : zero4;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+          const uint32_t word = wq[c][(t + u) >> 2][(t + u) & 3];
+          f32x4* ac = acc[u % AU][c];
+          if constexpr (MODE == MODE_B2) {
+            ac[0] = mfma16x16x32(a, expand_nat(word, h, sh, mh[u]), ac[0]);
+            ac[1] = mfma16x16x32(a, expand_nat(word, h, sh, ml[u]), ac[1]);
+          } else {
+            ac[0] = mfma16x16x32(a, expand_nat(word, h, sh, ones), ac[0]);
+          }
+        }
+      }
+    }
+  }
+
+  // Fixed summation order: terms of a set, then the sets in order.
+  f32x4 tot[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    tot[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      f32x4 su = acc[u][c][0];
+#pragma unroll
+      for (int a = 1; a < NA; ++a) su = su + acc[u][c][a];
+      tot[c] = tot[c] + su;
+    }
+  }
+  // Waves' sums through LDS: red[wave][row][column]; lane holds rows 4g .. 4g+3
+  // of column 16c + j.  Added in wave order.
+  __syncthreads();   // every wave is done with its staging region
+  float* red = reinterpret_cast<float*>(wk_lds);
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * g + i) * RS + 16 * c + j] = tot[c][i];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NOUT; ++r) {
+    const int o = tid + WK_THREADS * r;
+    const int m = o / NC, cl = o - (o / NC) * NC;
+    if (o < 16 * NC && m < M && n0 + cl < N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < WK_WAVES; ++w) v += red[(w * 16 + m) * RS + cl];
+      Store<YT>::put(&Y[(int64_t)m * N + n0 + cl], v * post_o[r]);
+    }
+  }
+}
+
+template <int MODE, typename ST, typename YT, int CPW>
+hipError_t launch_wk(const LinearArgs& a) {
+  const int64_t blocks = (a.N + 16 * CPW - 1) / (16 * CPW);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_wk_kernel<MODE, ST, YT, CPW>), dim3((unsigned)blocks), dim3(WK_THREADS),
+                     wk_lds_bytes(a.M, CPW), a.stream, static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N,
+                     static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post), static_cast<YT*>(a.Y));
+  return hipGetLastError();
+}
+
+// Columns per wave of the whole-K variant, or 0 for the split kernel.
+// OBL_DECODE=split|wk1|wk2|wk4 forces a choice (tests cover each).
+int wk_columns_per_wave(const LinearArgs& a, const DeviceInfo& dev) {
+  const char* e = std::getenv("OBL_DECODE");
+  if (e && !std::strcmp(e, "split")) return 0;
+  int cpw = 0;
+  if (e && e[0] == 'w' && e[1] == 'k' && (e[2] == '1' || e[2] == '2' || e[2] == '4') && !e[3]) cpw = e[2] - '0';
+  if (cpw == 0) {
+    // Default: the fewest columns per wave that keep the grid within one
+    // workgroup per CU (the 16-row staging takes most of a CU's LDS, so a
+    // second round of workgroups pays the whole latency chain again).
+    // Same-box timings, us per call, CPW = 1 / 2 / 4: 16 x 4096 x 4096
+    // 6.4 / 8.0 / 11.4; 16 x 4096 x 14336 20.8 / 14.7 / 11.7; 16 x 4096 x
+    // 11008 16.1 / 14.4 / 11.5 (the split kernel: 8.4, 16.7, 14.6).
+    const int64_t cols = (a.N + 15) / 16;
+    cpw = cols <= dev.num_cus ? 1 : (cols <= 2 * dev.num_cus ? 2 : 4);
+  }
+  return cpw;
+}
+
+bool wk_eligible(const LinearArgs& a, bool raw_mode) {
+  return raw_mode && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+}
+
+template <int MODE, typename ST, typename YT>
+hipError_t launch_wk_any(const LinearArgs& a, int cpw) {
+  if (cpw == 4) return launch_wk<MODE, ST, YT, 4>(a);
+  if (cpw == 2) return launch_wk<MODE, ST, YT, 2>(a);
+  return launch_wk<MODE, ST, YT, 1>(a);
+}
+
 template <int MODE, typename XT, typename ST, typename YT, bool PRE>
 hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
   const int64_t kw = a.K / 32;
@@ -392,8 +634,15 @@ template <typename ST, typename YT>
 hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
   // bf16 x: A is x itself (any alignment: the staging copies it to LDS).
   const bool raw = a.x_dtype == DT_BF16;
-  if (raw && !a.pre) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
-  if (raw && a.scale_dtype == DT_F16) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);
+  const bool b1 = raw && !a.pre, b2 = raw && a.pre && a.scale_dtype == DT_F16;
+  // (Every public entry point passes an input-side scale, so only mode B2
+  // reaches the whole-K variant.)
+  if (wk_eligible(a, b2)) {
+    const int cpw = wk_columns_per_wave(a, dev);
+    if (cpw > 0) return launch_wk_any<MODE_B2, ST, YT>(a, cpw);
+  }
+  if (b1) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
+  if (b2) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);
   if (a.x_dtype == DT_BF16)
     return a.pre ? launch_t<MODE_S3, bf16_t, ST, YT, true>(a, dev)
                  : launch_t<MODE_S3, bf16_t, ST, YT, false>(a, dev);
