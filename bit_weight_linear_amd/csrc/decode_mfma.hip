@@ -51,6 +51,7 @@
 // issued before the first MFMA and each step owns its accumulators.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "obl_common.hpp"
 #include "obl_internal.hpp"
@@ -360,42 +361,76 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Whole-K variant (bf16 x and fp16 b: mode B2; 16-byte aligned X and W, K %
-// 128 == 0).  A workgroup of 8 waves owns 16·CPW output columns over all of K;
-// wave w takes the 512-k slices w, w + 8, ... of them.  Per slice the wave
-// stages its M rows of X in its own LDS region (one 1 KiB DMA per row, the
-// same swizzle as above), loads its columns' 16 sign words per column straight
-// into registers (the four lanes of a column load the same words), builds the
-// slice's (b_hi, b_lo) pair tables, and contracts the slice as above; no
-// workgroup barrier is needed until the end, where the eight per-wave sums of
-// each output are added in wave order through LDS and the post scale applied.
-// One launch, and no partial sums through HBM: the split-K kernel needs a
-// second launch for its slice reduction, which must wait for the first.  The
-// price is that every workgroup reads all of X (M·K·2 bytes through its CU).
-// With one column group per wave and K <= 4096 (one slice per wave) the sums
-// are added in exactly the split kernel's order: both give bitwise the same
-// results.
+// Whole-K variant (bf16 x and fp16 b, mode B2; 16-byte aligned X, W and b,
+// K % 128 == 0).  A workgroup of 8 waves owns 16·CPW output columns over all
+// of K; wave w takes the 512-k slices w, w + 8, ... of them.  Per slice the
+// wave copies into its own LDS region, by DMA and in this order: the slice's
+// sign words of its columns, the slice's b, and its M rows of X by k-quarter
+// (128 k); it then contracts quarter q as soon as quarters <= q have landed,
+// so the contraction overlaps the rest of the copy.  No workgroup barrier is
+// needed until the end, where the eight per-wave sums of each output are
+// added in wave order through LDS and the post scale applied.  One launch,
+// and no partial sums through HBM: the split-K kernel needs a second launch
+// for its slice reduction, which must wait for the first.  The price is that
+// every workgroup reads all of X (M·K·2 bytes through its CU).  With one
+// column group per wave and K <= 4096 (one slice per wave) the sums are added
+// in exactly the split kernel's order: both give bitwise the same results.
+//
+// Every transfer of the slice is an LDS DMA, waited for with explicit vmcnt
+// counts: a load into registers issued before the DMAs is waited for with
+// vmcnt(0) at its first use (the compiler's count of transfers in flight
+// does not include LDS DMAs), which would serialise the copy and the
+// contraction.  Only where the sign words do not fit in LDS next to 16 rows
+// of X (CPW = 4 with M > 8) are they loaded into registers, at that cost.
 constexpr int WK_WAVES = 8;
 constexpr int WK_THREADS = 64 * WK_WAVES;
+constexpr size_t WK_LDS_MAX = 160 * 1024;
 
-// LDS of one wave (16-byte units): M rows x 64 X chunks, then 64 b_hi and 64
-// b_lo pair quads.  After the contraction the area holds the reduction table.
-__host__ __device__ inline size_t wk_wave_units(int64_t M) { return (size_t)M * 64 + 128; }
-inline size_t wk_lds_bytes(int64_t M, int cpw) {
-  const size_t stage = (size_t)WK_WAVES * wk_wave_units(M) * 16;
+// LDS of one wave, in 16-byte units: X as four k-quarters, each [4·PER rows]
+// [16 chunks] (PER = DMAs of 4 rows per quarter, a template constant so the
+// waits are immediates); 64 b_hi pair quads and 64 b_lo pair quads (the raw
+// fp16 b of the slice lands in the b_lo area first); then, when they fit, the
+// sign words as [CPW][quarter][16 columns].  After the contraction the area
+// holds the reduction table.
+__host__ __device__ constexpr size_t wk_wave_units_nosigns(int per) { return (size_t)per * 256 + 128; }
+__host__ __device__ constexpr bool wk_signs_in_lds(int per, int cpw) {
+  return (size_t)WK_WAVES * (wk_wave_units_nosigns(per) + 64 * (size_t)cpw) * 16 <= WK_LDS_MAX;
+}
+__host__ __device__ constexpr size_t wk_wave_units(int per, int cpw) {
+  return wk_wave_units_nosigns(per) + (wk_signs_in_lds(per, cpw) ? 64 * (size_t)cpw : 0);
+}
+inline int wk_per(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
+inline size_t wk_lds_bytes(int per, int cpw) {
+  const size_t stage = (size_t)WK_WAVES * wk_wave_units(per, cpw) * 16;
   const size_t red = (size_t)WK_WAVES * 16 * (16 * cpw + 1) * sizeof(float);
   return stage > red ? stage : red;
 }
 
-template <int MODE, typename ST, typename YT, int CPW>
+// Wait until at most N of this wave's vector-memory transfers are in flight.
+template <int N>
+__device__ __forceinline__ void wk_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
+
+// Order this wave's LDS writes before its later LDS reads (only this wave
+// touches its region: no workgroup barrier).
+__device__ __forceinline__ void wk_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename ST, typename YT, int CPW, int PER>
 __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
-    const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y) {
-  static_assert(MODE == MODE_B1 || MODE == MODE_B2, "bf16 activations only");
-  constexpr int NA = MODE == MODE_B1 ? 1 : 2;
+    const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y) {
   constexpr int NC = 16 * CPW;                                    // columns per workgroup
   constexpr int RS = NC + 1;                                      // reduction table row stride (floats)
   constexpr int NOUT = (16 * NC + WK_THREADS - 1) / WK_THREADS;   // final outputs per thread
+  constexpr int M4 = 4 * PER;                                     // X rows staged (>= M)
+  constexpr bool SL = wk_signs_in_lds(PER, CPW);                  // sign words by DMA into LDS
+  constexpr int NSIG = SL ? CPW : 0;                              // sign DMAs per slice
   extern __shared__ u32x4 wk_lds[];
 
   const int tid = threadIdx.x;
@@ -406,8 +441,28 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   const int64_t kw = K >> 5;
   const int nslices = (int)((kw + DEC_STEPS - 1) / DEC_STEPS);
   const int64_t n0 = (int64_t)blockIdx.x * NC;
-  u32x4* xw = wk_lds + (size_t)wave * wk_wave_units(M);          // this wave's X chunks
-  uint32_t* mw = reinterpret_cast<uint32_t*>(xw + (size_t)M * 64);   // b_hi pairs [256], b_lo pairs [256]
+  u32x4* xw = wk_lds + (size_t)wave * wk_wave_units(PER, CPW);   // X quarters
+  u32x4* mq = xw + M4 * 64;                                       // b_hi quads [64], b_lo quads [64]
+  uint32_t* mw = reinterpret_cast<uint32_t*>(mq);
+  u32x4* sg = mq + 128;                                           // sign quads [CPW][4][16] (SL)
+  // Buffer resources: offsets past the end of X, W or b read zeros, so the
+  // DMAs need no clamping (what they read past the last slice's K is masked).
+  // Byte offsets fit in 32 bits (checked by the launcher).
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(N * kw * 4));
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(pre, (uint32_t)(K * 2));
+  // Per-lane DMA offsets, fixed over the slices: X row group i (row 4i +
+  // lane / 16, chunk (lane % 16) ^ (row % 16) of a quarter), sign quad lane / 16
+  // of column 16c + lane % 16, b chunk lane.
+  uint32_t xo[PER], so[SL ? CPW : 1];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    xo[i] = (uint32_t)((min(row, M - 1) * K + 8 * ((lane & 15) ^ (row & 15))) * 2);
+  }
+#pragma unroll
+  for (int c = 0; c < (SL ? CPW : 1); ++c)
+    so[c] = (uint32_t)((min(n0 + 16 * c + j, N - 1) * kw + 4 * (lane >> 4)) * 4);
 
   // Output scales of this thread's final outputs (o = tid + WK_THREADS r is
   // row o / NC, column o % NC), issued before the streams.
@@ -424,9 +479,8 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   }
   const int h = g >> 1;
   const bool mrow = j < M;
-  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  const int xrow = (mrow ? j : 0) * 64;
+  const int xrow = (mrow ? j : 0) * 16;
   const int swz = j & 15;
 
   // Accumulator sets: step t adds into set t % AU.  With one column group
@@ -434,89 +488,99 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   // with more, the column groups already give the MFMAs enough independent
   // chains and fewer sets keep the registers within two waves per SIMD.
   constexpr int AU = CPW == 1 ? 4 : (CPW == 2 ? 2 : 1);
-  f32x4 acc[AU][CPW][NA];
+  f32x4 acc[AU][CPW][2];
 #pragma unroll
   for (int u = 0; u < AU; ++u)
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-      for (int a = 0; a < NA; ++a) acc[u][c][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CPW; ++c) acc[u][c][0] = acc[u][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int s = wave; s < nslices; s += WK_WAVES) {
     const int64_t step0 = (int64_t)s * DEC_STEPS;
     const int64_t k0 = step0 * 32;
     const int nsteps = (int)min((int64_t)DEC_STEPS, kw - step0);   // a multiple of 4
-    // X: row r by one DMA, lane l -> slot l = chunk l ^ (r % 16); chunks past
-    // K re-read chunk 0 of the slice (never used).
-    for (int r = 0; r < M; ++r) {
-      int64_t ke = k0 + 8 * (int64_t)(lane ^ (r & 15));
-      if (ke >= K) ke = k0;
-      load_lds16(X + (int64_t)r * K + ke, xw + r * 64);
-    }
-    // Sign words: all 16 of the slice for each of this lane's columns; quads
-    // past the end re-read quad 0 (masked below).
-    u32x4 wq[CPW][4];
+    // Sign words of the slice: quad q (steps 4q .. 4q+3) of column 16c + i.
+    // SL: DMA c, lane l -> quad l / 16 of column l % 16, at sg[c][l / 16][l % 16];
+    // otherwise the four lanes of a column load all four quads.  Quads past
+    // the end re-read quad 0 (masked below).
+    u32x4 wq[SL ? 1 : CPW][4];
+    if constexpr (SL) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const uint32_t* src = W + min(n0 + 16 * c + j, N - 1) * kw + step0;
+      for (int c = 0; c < CPW; ++c) dma16(wr, sg + 64 * c, so[c], (uint32_t)(step0 * 4));
+    } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wq[c][q] = *reinterpret_cast<const u32x4*>(src + (4 * q < nsteps ? 4 * q : 0));
-    }
-    // Mode B2: b pairs (lane + 64 i) of the slice.
-    float bp[4][2];
-    if constexpr (MODE == MODE_B2) {
+      for (int c = 0; c < CPW; ++c) {
+        const uint32_t* src = W + min(n0 + 16 * c + j, N - 1) * kw + step0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t k = k0 + 2 * (lane + 64 * i);
-        const int64_t kc = k < K ? k : 0;
-        bp[i][0] = to_f32(pre[kc]);
-        bp[i][1] = to_f32(pre[kc + 1]);
-        if (k >= K) bp[i][0] = bp[i][1] = 0.f;
+        for (int q = 0; q < 4; ++q) wq[c][q] = *reinterpret_cast<const u32x4*>(src + (4 * q < nsteps ? 4 * q : 0));
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the slice is in LDS and registers
-    if constexpr (MODE == MODE_B2) {
+    // The waits below count transfers in issue order: scheduling barriers
+    // keep the compiler from reordering the groups.
+    __builtin_amdgcn_sched_barrier(0);
+    // b of the slice, raw fp16, lane l -> k0 + 8l .. +7 into the b_lo area
+    // (chunks past K re-read chunk 0; masked when converted).
+    dma16(br, mq + 64, (uint32_t)(16 * lane), (uint32_t)(k0 * 2));
+    __builtin_amdgcn_sched_barrier(0);
+    // X quarter q (k0 + 128q .. +127): DMA i writes rows 4i .. 4i+3, lane l ->
+    // row 4i + l/16, slot l % 16 = chunk (l % 16) ^ (row % 16) of the quarter.
+    // Rows past M re-read row M - 1 (never used).
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) dma16(xr, xw + (q * M4 + 4 * i) * 16, xo[i], (uint32_t)((k0 + 128 * q) * 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wk_wait_vm<3 * PER>();   // signs, b and quarter 0 landed
+    wk_wave_sync();
+    // b pairs -> (b_hi, b_lo) tables: dword p = lane + 64 i holds k0 + 2p and
+    // k0 + 2p + 1; every lane reads its four raw dwords before writing.
+    {
+      uint32_t raw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = mw[256 + lane + 64 * i];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float h0 = bf16_round(bp[i][0]), h1 = bf16_round(bp[i][1]);
-        mw[lane + 64 * i] = pack_bf16_pair(h0, h1);
-        mw[256 + lane + 64 * i] = pack_bf16_pair(bp[i][0] - h0, bp[i][1] - h1);   // exact (fp16 residual)
+        const int p = lane + 64 * i;
+        const bool in = k0 + 2 * p < K;
+        const float b0 = in ? to_f32(f16_t{(uint16_t)(raw[i] & 0xFFFFu)}) : 0.f;
+        const float b1 = in ? to_f32(f16_t{(uint16_t)(raw[i] >> 16)}) : 0.f;
+        const float h0 = bf16_round(b0), h1 = bf16_round(b1);
+        mw[p] = pack_bf16_pair(h0, h1);
+        mw[256 + p] = pack_bf16_pair(b0 - h0, b1 - h1);   // exact (fp16 residual)
       }
     }
-    // Only this wave writes and reads its region: order its LDS writes before
-    // its reads, no workgroup barrier.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wk_wave_sync();
 
 #pragma unroll
     for (int t = 0; t < DEC_STEPS; t += 4) {
-      u32x4 xf[4], mh[4], ml[4];
+      // Quarter t / 4: wait for its DMAs (the later quarters may still fly).
+      if (t == 4) wk_wait_vm<2 * PER>();
+      if (t == 8) wk_wait_vm<PER>();
+      if (t == 12) wk_wait_vm<0>();
+      if (t > 0) wk_wave_sync();
+      u32x4 xf[4], mh[4], ml[4], wv[CPW];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) wv[c] = SL ? sg[(4 * c + t / 4) * 16 + j] : wq[SL ? 0 : c][t / 4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int kb = 32 * (t + u) + 8 * g;
-        xf[u] = xw[xrow + ((kb / 8) ^ swz)];
-        if constexpr (MODE == MODE_B2) {
-          mh[u] = *reinterpret_cast<const u32x4*>(mw + kb / 2);
-          ml[u] = *reinterpret_cast<const u32x4*>(mw + 256 + kb / 2);
-        }
+        xf[u] = xw[(t / 4) * M4 * 16 + xrow + ((4 * u + g) ^ swz)];
+        mh[u] = mq[kb / 8];
+        ml[u] = mq[64 + kb / 8];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const u32x4 a = (mrow && (t + u < nsteps)) ? xf[u] : zero4;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
-          const uint32_t word = wq[c][(t + u) >> 2][(t + u) & 3];
+          const uint32_t word = wv[c][u];
           f32x4* ac = acc[u % AU][c];
-          if constexpr (MODE == MODE_B2) {
-            ac[0] = mfma16x16x32(a, expand_nat(word, h, sh, mh[u]), ac[0]);
-            ac[1] = mfma16x16x32(a, expand_nat(word, h, sh, ml[u]), ac[1]);
-          } else {
-            ac[0] = mfma16x16x32(a, expand_nat(word, h, sh, ones), ac[0]);
-          }
+          ac[0] = mfma16x16x32(a, expand_nat(word, h, sh, mh[u]), ac[0]);
+          ac[1] = mfma16x16x32(a, expand_nat(word, h, sh, ml[u]), ac[1]);
         }
       }
     }
+    wk_wave_sync();   // the next slice's DMAs overwrite this slice's LDS
   }
 
   // Fixed summation order: terms of a set, then the sets in order.
@@ -525,12 +589,7 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   for (int c = 0; c < CPW; ++c) {
     tot[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < AU; ++u) {
-      f32x4 su = acc[u][c][0];
-#pragma unroll
-      for (int a = 1; a < NA; ++a) su = su + acc[u][c][a];
-      tot[c] = tot[c] + su;
-    }
+    for (int u = 0; u < AU; ++u) tot[c] = tot[c] + (acc[u][c][0] + acc[u][c][1]);
   }
   // Waves' sums through LDS: red[wave][row][column]; lane holds rows 4g .. 4g+3
   // of column 16c + j.  Added in wave order.
@@ -554,14 +613,22 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   }
 }
 
-template <int MODE, typename ST, typename YT, int CPW>
+template <typename ST, typename YT, int CPW, int PER>
 hipError_t launch_wk(const LinearArgs& a) {
   const int64_t blocks = (a.N + 16 * CPW - 1) / (16 * CPW);
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_wk_kernel<MODE, ST, YT, CPW>), dim3((unsigned)blocks), dim3(WK_THREADS),
-                     wk_lds_bytes(a.M, CPW), a.stream, static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N,
-                     static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post), static_cast<YT*>(a.Y));
+  if (blocks > 0x7fffffff || a.M > 4 * PER) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_wk_kernel<ST, YT, CPW, PER>), dim3((unsigned)blocks), dim3(WK_THREADS),
+                     wk_lds_bytes(PER, CPW), a.stream, static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N,
+                     static_cast<const f16_t*>(a.pre), static_cast<const ST*>(a.post), static_cast<YT*>(a.Y));
   return hipGetLastError();
+}
+
+template <typename ST, typename YT, int CPW>
+hipError_t launch_wk_rows(const LinearArgs& a) {
+  const int per = wk_per(a.M);
+  if (per == 1) return launch_wk<ST, YT, CPW, 1>(a);
+  if (per == 2) return launch_wk<ST, YT, CPW, 2>(a);
+  return launch_wk<ST, YT, CPW, 4>(a);
 }
 
 // Columns per wave of the whole-K variant, or 0 for the split kernel.
@@ -584,16 +651,20 @@ int wk_columns_per_wave(const LinearArgs& a, const DeviceInfo& dev) {
   return cpw;
 }
 
-bool wk_eligible(const LinearArgs& a, bool raw_mode) {
-  return raw_mode && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
-         reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+// Mode B2 with every operand the kernel DMAs 16-byte aligned.
+bool wk_eligible(const LinearArgs& a, bool b2) {
+  // Buffer byte ranges (and offsets, with one slice to spare) within 32 bits.
+  const int64_t lim = (int64_t)0xFFFFF000u - 4096;
+  return b2 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && reinterpret_cast<uintptr_t>(a.pre) % 16 == 0 &&
+         a.M * a.K * 2 <= lim && a.N * (a.K / 32) * 4 <= lim;
 }
 
-template <int MODE, typename ST, typename YT>
+template <typename ST, typename YT>
 hipError_t launch_wk_any(const LinearArgs& a, int cpw) {
-  if (cpw == 4) return launch_wk<MODE, ST, YT, 4>(a);
-  if (cpw == 2) return launch_wk<MODE, ST, YT, 2>(a);
-  return launch_wk<MODE, ST, YT, 1>(a);
+  if (cpw == 4) return launch_wk_rows<ST, YT, 4>(a);
+  if (cpw == 2) return launch_wk_rows<ST, YT, 2>(a);
+  return launch_wk_rows<ST, YT, 1>(a);
 }
 
 template <int MODE, typename XT, typename ST, typename YT, bool PRE>
@@ -637,9 +708,11 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
   const bool b1 = raw && !a.pre, b2 = raw && a.pre && a.scale_dtype == DT_F16;
   // (Every public entry point passes an input-side scale, so only mode B2
   // reaches the whole-K variant.)
-  if (wk_eligible(a, b2)) {
-    const int cpw = wk_columns_per_wave(a, dev);
-    if (cpw > 0) return launch_wk_any<MODE_B2, ST, YT>(a, cpw);
+  if constexpr (std::is_same<ST, f16_t>::value) {
+    if (wk_eligible(a, b2)) {
+      const int cpw = wk_columns_per_wave(a, dev);
+      if (cpw > 0) return launch_wk_any<ST, YT>(a, cpw);
+    }
   }
   if (b1) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
   if (b2) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);

@@ -74,12 +74,6 @@ constexpr int GW_FM = GW_WM / 32; // 2 activation fragments
 constexpr int GW_KT = 128;        // k per stage
 constexpr int GW_S = GW_KT / 16;  // MFMA k-steps per stage
 
-// Buffer resource for a raw byte range (loads past `bytes` would return zeros;
-// the kernel clamps its offsets so none does).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -96,14 +90,6 @@ __device__ __forceinline__ u32x4 expand_half(uint32_t h, const u16x2* sh, u32x4 
   r.z = (__builtin_bit_cast(uint32_t, d << sh[2]) & 0x80008000u) ^ mag.z;
   r.w = (__builtin_bit_cast(uint32_t, d << sh[3]) & 0x80008000u) ^ mag.w;
   return r;
-}
-
-// LDS DMA of 16 bytes per lane from a buffer resource: lane l's bytes land at
-// lds_wave_base + 16 l (lds_wave_base uniform over the wave).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff,
-                                      uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
-                                           (int)voff, (int)soff, 0, 0);
 }
 
 constexpr int GW_XDMA = GW_BM * (GW_KT / 8) / 64 / 4;    // activation DMAs per wave per stage (8)

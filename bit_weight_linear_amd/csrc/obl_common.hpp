@@ -70,6 +70,21 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
+// Buffer resource for a raw byte range: loads past `bytes` return zeros
+// instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// LDS DMA of 16 bytes per lane from a buffer resource at byte offset voff +
+// soff (soff uniform): lane l's bytes land at lds_wave_base + 16 l
+// (lds_wave_base uniform over the wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)voff, (int)soff, 0, 0);
+}
+
 // Workgroup barrier that makes this wave's LDS writes visible but does not
 // wait for its global loads in flight (__syncthreads() also drains vmcnt).
 // s_waitcnt immediate: lgkmcnt = 0, vmcnt = 63 and expcnt = 7 (no wait).
