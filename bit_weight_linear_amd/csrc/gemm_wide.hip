@@ -98,8 +98,9 @@ constexpr double GW_EFF4 = 1.08;                          // per-column cost of 
 
 // Column tiling, by sign fragments (32 columns) per wave: FN = 7 gives the
 // 64 x 224 wave tile and 128 x 448 workgroup tile, FN = 4 a 64 x 128 wave
-// tile and 128 x 256 workgroup tile.  Sign columns are staged in whole
-// 256-column DMA rounds (one 16-byte DMA per lane per round).
+// tile and 128 x 256 workgroup tile, FN = 2 a 64 x 64 wave tile and 128 x 128
+// workgroup tile.  Sign columns are staged in whole 256-column DMA rounds
+// (one 16-byte DMA per lane per round; the 128-wide tile uses half of it).
 template <int FN> struct GwTile {
   static constexpr int WN = 32 * FN;                      // wave columns
   static constexpr int BN = 2 * WN;                       // workgroup columns
@@ -464,13 +465,18 @@ hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
   return hipGetLastError();
 }
 
-// Column-tile width.  A grid that splits K with the 256-wide tile takes it
-// (more tiles, fewer slices: less partial-sum traffic; measured at M = 512:
-// 512x4096x3072 30.5 vs 38.4 us).  Otherwise the estimated time is the number
-// of rounds of one workgroup per CU times the tile width, with `GW_EFF4` the
-// relative per-column cost of the narrow tile.  Measured at M = 2048, K = 4096:
-// N = 14336 keeps 448 (217 vs 245 us), N = 11008 and N = 4096 take 256
-// (182 vs 198 us, 67 vs 96 us).  OBL_GEMM=w4 / w7 forces a width (tests).
+// Column-tile width.  A grid that would split K with the 256-wide tile takes
+// the 128-wide one (twice the tiles, half the slices: half the partial-sum
+// traffic).  Same-box timings, 128 vs 256 vs 448 wide, us: 512x3072x4096
+// 30.2 / 33.2 / 37.2, 512x4096x4096 32.8 / 35.9 / 41.6, 1024x4096x4096
+// 39.7 / 47.2 / 55.9, 256x4096x4096 26.1 / 32.5 / 36.7, 512x4096x3072
+// 31.1 / 30.4 / 38.3, the DBF prefill 512x4096->3072->4096 61.2 / 64.7 /
+// 78.3.  Otherwise the estimated time is the number of rounds of one
+// workgroup per CU times the tile width, with `GW_EFF4` the relative
+// per-column cost of the 256-wide tile against the 448-wide one.  Measured at
+// M = 2048, K = 4096: N = 14336 keeps 448 (217 vs 245 us), N = 11008 and
+// N = 4096 take 256 (182 vs 198 us, 67 vs 96 us; the 128-wide tile 77 us).
+// OBL_GEMM=w2 / w4 / w7 forces a width (tests).
 int64_t rounds(int64_t M, int64_t N, int bn, int cus) {
   const int64_t tiles = ((M + GW_BM - 1) / GW_BM) * ((N + bn - 1) / bn);
   return (tiles + cus - 1) / cus;
@@ -478,10 +484,11 @@ int64_t rounds(int64_t M, int64_t N, int bn, int cus) {
 
 int pick_fn(int64_t M, int64_t N, int cus) {
   const char* e = std::getenv("OBL_GEMM");
+  if (e && e[0] == 'w' && e[1] == '2') return 2;
   if (e && e[0] == 'w' && e[1] == '4') return 4;
   if (e && e[0] == 'w' && e[1] == '7') return 7;
   const int64_t tiles4 = ((M + GW_BM - 1) / GW_BM) * ((N + GwTile<4>::BN - 1) / GwTile<4>::BN);
-  if (tiles4 * 2 <= cus) return 4;
+  if (tiles4 * 2 <= cus) return 2;
   const double u4 = (double)rounds(M, N, GwTile<4>::BN, cus) * GwTile<4>::BN * GW_EFF4;
   const double u7 = (double)rounds(M, N, GwTile<7>::BN, cus) * GwTile<7>::BN;
   return u4 < u7 ? 4 : 7;
@@ -489,7 +496,9 @@ int pick_fn(int64_t M, int64_t N, int cus) {
 
 template <typename ST, typename YT, bool PRE>
 hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
-  return pick_fn(a.M, a.N, dev.num_cus) == 4 ? launch_fn<ST, YT, PRE, 4>(a, dev) : launch_fn<ST, YT, PRE, 7>(a, dev);
+  const int fn = pick_fn(a.M, a.N, dev.num_cus);
+  if (fn == 2) return launch_fn<ST, YT, PRE, 2>(a, dev);
+  return fn == 4 ? launch_fn<ST, YT, PRE, 4>(a, dev) : launch_fn<ST, YT, PRE, 7>(a, dev);
 }
 
 template <typename ST>
@@ -603,7 +612,7 @@ bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const voi
   // out-of-range sentinel), and the grid in an int.
   const int64_t lim = (int64_t)0xFFFFF000u;
   if (a.M * a.K * 2 > lim || a.N * (a.K / 32) * 4 > lim) return false;
-  const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GwTile<4>::BN - 1) / GwTile<4>::BN);
+  const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GwTile<2>::BN - 1) / GwTile<2>::BN);
   if (tiles > 0x7fffffff) return false;
   // LDS: the bf16(b) table (2K bytes rounded up to 8 KiB batches, dynamic)
   // next to ~124 KiB of static stage buffers.

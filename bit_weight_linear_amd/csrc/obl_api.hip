@@ -74,10 +74,12 @@ Path forced_path() {
   return P_AUTO;
 }
 
-// OBL_GEMM set (tests forcing a GEMM kernel): keep stage 2 on the fp32 workspace.
+// OBL_GEMM=v1|v2 (tests forcing an older GEMM kernel, which cannot write the
+// bf16 copy of T1): keep stage 2 on the fp32 workspace.  The w* settings only
+// pick a tile width of the main kernel.
 bool gemm_forced_any() {
   const char* e = std::getenv("OBL_GEMM");
-  return e && e[0];
+  return e && e[0] == 'v';
 }
 
 Path choose_path(int64_t M, obl_status* st) {
