@@ -365,7 +365,7 @@ def main():
         sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
                         "algorithmic_bytes": int(ab5), "ideal_us_hbm": round(ab5 / HBM_PEAK_GBS / 1e3, 4),
                         "hbm_frac": round(ab5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "bound": "latency (two stages, four launches)",
+                        "bound": "latency (two stages, three launches: stage 2 on the fp32 T1 splits K)",
                         "check_vs_torch_fp32": float(f"{e5:.3e}"), "copies": R5,
                         "stages_per_call": 2}
         log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
@@ -382,7 +382,7 @@ def main():
                         "check_vs_torch_fp32": float(f"{e6:.3e}"), "copies": R6}
         log(f"[bench] {c6.name}: {ms6 * 1e3:.1f} us per call, {tf6:.1f} TFLOP/s")
         del l6, t6
-        # backward of the layer at the batched-decode shape (two sign contractions + reductions)
+        # backward of the layer at the batched-decode shape (two sign contractions + the grads kernel)
         l7, e7 = backward_setup(torch, B, WL, 16, 4096, 4096, copies=64)
         assert e7 <= 1e-4, "the backward disagrees with the fp32 guard"
         t7 = Timed(torch, l7)
