@@ -362,14 +362,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // Whole-K variant (bf16 x and fp16 b, mode B2; 16-byte aligned X, W and b,
-// K % 128 == 0).  A workgroup of 8 waves owns 16·CPW output columns over all
-// of K; wave w takes the 512-k slices w, w + 8, ... of them.  Per slice the
+// K % 128 == 0; up to 32 rows).  A workgroup of 8 waves (4 for 17..32 rows,
+// whose X slices take twice the LDS) owns 16·CPW output columns over all of
+// K; wave w takes the 512-k slices w, w + W, ... of them (W waves).  Rows come
+// in fragments of 16 (one MFMA A operand each): a 32-row call contracts two
+// fragments against every expanded sign operand.  Per slice the
 // wave copies into its own LDS region, by DMA and in this order: the slice's
 // sign words of its columns, the slice's b, and its M rows of X by k-quarter
 // (128 k); it then contracts quarter q as soon as quarters <= q have landed,
 // so the contraction overlaps the rest of the copy.  No workgroup barrier is
-// needed until the end, where the eight per-wave sums of each output are
-// added in wave order through LDS and the post scale applied.  One launch,
+// needed until the end, where the per-wave sums of each output are added in
+// wave order through LDS and the post scale applied.  One launch,
 // and no partial sums through HBM: the split-K kernel needs a second launch
 // for its slice reduction, which must wait for the first.  The price is that
 // every workgroup reads all of X (M·K·2 bytes through its CU).  With one
@@ -380,11 +383,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // counts: a load into registers issued before the DMAs is waited for with
 // vmcnt(0) at its first use (the compiler's count of transfers in flight
 // does not include LDS DMAs), which would serialise the copy and the
-// contraction.  Only where the sign words do not fit in LDS next to 16 rows
+// contraction.  Only where the sign words do not fit in LDS next to the rows
 // of X (CPW = 4 with M > 8) are they loaded into registers, at that cost.
-constexpr int WK_WAVES = 8;
-constexpr int WK_THREADS = 64 * WK_WAVES;
 constexpr size_t WK_LDS_MAX = 160 * 1024;
+__host__ __device__ constexpr int wk_waves(int per) { return per == 8 ? 4 : 8; }
 
 // LDS of one wave, in 16-byte units: X as four k-quarters, each [4·PER rows]
 // [16 chunks] (PER = DMAs of 4 rows per quarter, a template constant so the
@@ -394,15 +396,15 @@ constexpr size_t WK_LDS_MAX = 160 * 1024;
 // holds the reduction table.
 __host__ __device__ constexpr size_t wk_wave_units_nosigns(int per) { return (size_t)per * 256 + 128; }
 __host__ __device__ constexpr bool wk_signs_in_lds(int per, int cpw) {
-  return (size_t)WK_WAVES * (wk_wave_units_nosigns(per) + 64 * (size_t)cpw) * 16 <= WK_LDS_MAX;
+  return (size_t)wk_waves(per) * (wk_wave_units_nosigns(per) + 64 * (size_t)cpw) * 16 <= WK_LDS_MAX;
 }
 __host__ __device__ constexpr size_t wk_wave_units(int per, int cpw) {
   return wk_wave_units_nosigns(per) + (wk_signs_in_lds(per, cpw) ? 64 * (size_t)cpw : 0);
 }
-inline int wk_per(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
+inline int wk_per(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : (M <= 16 ? 4 : 8)); }
 inline size_t wk_lds_bytes(int per, int cpw) {
-  const size_t stage = (size_t)WK_WAVES * wk_wave_units(per, cpw) * 16;
-  const size_t red = (size_t)WK_WAVES * 16 * (16 * cpw + 1) * sizeof(float);
+  const size_t stage = (size_t)wk_waves(per) * wk_wave_units(per, cpw) * 16;
+  const size_t red = (size_t)wk_waves(per) * 4 * per * (16 * cpw + 1) * sizeof(float);
   return stage > red ? stage : red;
 }
 
@@ -422,13 +424,16 @@ __device__ __forceinline__ void wk_wave_sync() {
 }
 
 template <typename ST, typename YT, int CPW, int PER>
-__global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
+__global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y) {
+  constexpr int WAVES = wk_waves(PER);
+  constexpr int THREADS = 64 * WAVES;
   constexpr int NC = 16 * CPW;                                    // columns per workgroup
   constexpr int RS = NC + 1;                                      // reduction table row stride (floats)
-  constexpr int NOUT = (16 * NC + WK_THREADS - 1) / WK_THREADS;   // final outputs per thread
   constexpr int M4 = 4 * PER;                                     // X rows staged (>= M)
+  constexpr int RF = (M4 + 15) / 16;                              // 16-row fragments
+  constexpr int NOUT = (16 * RF * NC + THREADS - 1) / THREADS;    // final outputs per thread
   constexpr bool SL = wk_signs_in_lds(PER, CPW);                  // sign words by DMA into LDS
   constexpr int NSIG = SL ? CPW : 0;                              // sign DMAs per slice
   extern __shared__ u32x4 wk_lds[];
@@ -464,12 +469,12 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   for (int c = 0; c < (SL ? CPW : 1); ++c)
     so[c] = (uint32_t)((min(n0 + 16 * c + j, N - 1) * kw + 4 * (lane >> 4)) * 4);
 
-  // Output scales of this thread's final outputs (o = tid + WK_THREADS r is
+  // Output scales of this thread's final outputs (o = tid + THREADS r is
   // row o / NC, column o % NC), issued before the streams.
   float post_o[NOUT];
 #pragma unroll
   for (int r = 0; r < NOUT; ++r)
-    post_o[r] = scale_or_one(post, min(n0 + (tid + WK_THREADS * r) % NC, N - 1), W);   // W: >= 4N bytes
+    post_o[r] = scale_or_one(post, min(n0 + (tid + THREADS * r) % NC, N - 1), W);   // W: >= 4N bytes
 
   u16x2 sh[4];
 #pragma unroll
@@ -478,9 +483,14 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
     sh[r] = u16x2{(unsigned short)(15 - p), (unsigned short)(14 - p)};
   }
   const int h = g >> 1;
-  const bool mrow = j < M;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  const int xrow = (mrow ? j : 0) * 16;
+  bool mrow[RF];                                                  // row 16f + j of fragment f exists
+  int xrow[RF];
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    mrow[f] = 16 * f + j < M;
+    xrow[f] = (mrow[f] ? 16 * f + j : 0) * 16;
+  }
   const int swz = j & 15;
 
   // Accumulator sets: step t adds into set t % AU.  With one column group
@@ -488,13 +498,15 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   // with more, the column groups already give the MFMAs enough independent
   // chains and fewer sets keep the registers within two waves per SIMD.
   constexpr int AU = CPW == 1 ? 4 : (CPW == 2 ? 2 : 1);
-  f32x4 acc[AU][CPW][2];
+  f32x4 acc[AU][CPW][RF][2];
 #pragma unroll
   for (int u = 0; u < AU; ++u)
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) acc[u][c][0] = acc[u][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) acc[u][c][f][0] = acc[u][c][f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = wave; s < nslices; s += WK_WAVES) {
+  for (int s = wave; s < nslices; s += WAVES) {
     const int64_t step0 = (int64_t)s * DEC_STEPS;
     const int64_t k0 = step0 * 32;
     const int nsteps = (int)min((int64_t)DEC_STEPS, kw - step0);   // a multiple of 4
@@ -558,25 +570,33 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
       if (t == 8) wk_wait_vm<PER>();
       if (t == 12) wk_wait_vm<0>();
       if (t > 0) wk_wave_sync();
-      u32x4 xf[4], mh[4], ml[4], wv[CPW];
+      u32x4 xf[4][RF], mh[4], ml[4], wv[CPW];
 #pragma unroll
       for (int c = 0; c < CPW; ++c) wv[c] = SL ? sg[(4 * c + t / 4) * 16 + j] : wq[SL ? 0 : c][t / 4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int kb = 32 * (t + u) + 8 * g;
-        xf[u] = xw[(t / 4) * M4 * 16 + xrow + ((4 * u + g) ^ swz)];
+#pragma unroll
+        for (int f = 0; f < RF; ++f) xf[u][f] = xw[(t / 4) * M4 * 16 + xrow[f] + ((4 * u + g) ^ swz)];
         mh[u] = mq[kb / 8];
         ml[u] = mq[64 + kb / 8];
       }
+      __builtin_amdgcn_sched_barrier(0);   // every LDS read of the quarter before its first MFMA
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const u32x4 a = (mrow && (t + u < nsteps)) ? xf[u] : zero4;
+        u32x4 a[RF];
+#pragma unroll
+        for (int f = 0; f < RF; ++f) a[f] = (mrow[f] && (t + u < nsteps)) ? xf[u][f] : zero4;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
           const uint32_t word = wv[c][u];
-          f32x4* ac = acc[u % AU][c];
-          ac[0] = mfma16x16x32(a, expand_nat(word, h, sh, mh[u]), ac[0]);
-          ac[1] = mfma16x16x32(a, expand_nat(word, h, sh, ml[u]), ac[1]);
+          const u32x4 bh = expand_nat(word, h, sh, mh[u]), bl = expand_nat(word, h, sh, ml[u]);
+#pragma unroll
+          for (int f = 0; f < RF; ++f) {
+            f32x4* ac = acc[u % AU][c][f];
+            ac[0] = mfma16x16x32(a[f], bh, ac[0]);
+            ac[1] = mfma16x16x32(a[f], bl, ac[1]);
+          }
         }
       }
     }
@@ -584,30 +604,34 @@ __global__ __launch_bounds__(WK_THREADS) void decode_wk_kernel(
   }
 
   // Fixed summation order: terms of a set, then the sets in order.
-  f32x4 tot[CPW];
+  f32x4 tot[CPW][RF];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    tot[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int u = 0; u < AU; ++u) tot[c] = tot[c] + (acc[u][c][0] + acc[u][c][1]);
-  }
-  // Waves' sums through LDS: red[wave][row][column]; lane holds rows 4g .. 4g+3
-  // of column 16c + j.  Added in wave order.
+    for (int f = 0; f < RF; ++f) {
+      tot[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < AU; ++u) tot[c][f] = tot[c][f] + (acc[u][c][f][0] + acc[u][c][f][1]);
+    }
+  // Waves' sums through LDS: red[wave][row][column]; lane holds rows
+  // 16f + 4g .. +3 of column 16c + j.  Added in wave order.
   __syncthreads();   // every wave is done with its staging region
   float* red = reinterpret_cast<float*>(wk_lds);
 #pragma unroll
   for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * g + i) * RS + 16 * c + j] = tot[c][i];
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(wave * 16 * RF + 16 * f + 4 * g + i) * RS + 16 * c + j] = tot[c][f][i];
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < NOUT; ++r) {
-    const int o = tid + WK_THREADS * r;
+    const int o = tid + THREADS * r;
     const int m = o / NC, cl = o - (o / NC) * NC;
-    if (o < 16 * NC && m < M && n0 + cl < N) {
+    if (o < 16 * RF * NC && m < M && n0 + cl < N) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < WK_WAVES; ++w) v += red[(w * 16 + m) * RS + cl];
+      for (int w = 0; w < WAVES; ++w) v += red[(w * 16 * RF + m) * RS + cl];
       Store<YT>::put(&Y[(int64_t)m * N + n0 + cl], v * post_o[r]);
     }
   }
@@ -617,7 +641,7 @@ template <typename ST, typename YT, int CPW, int PER>
 hipError_t launch_wk(const LinearArgs& a) {
   const int64_t blocks = (a.N + 16 * CPW - 1) / (16 * CPW);
   if (blocks > 0x7fffffff || a.M > 4 * PER) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_wk_kernel<ST, YT, CPW, PER>), dim3((unsigned)blocks), dim3(WK_THREADS),
+  hipLaunchKernelGGL((decode_wk_kernel<ST, YT, CPW, PER>), dim3((unsigned)blocks), dim3(64 * wk_waves(PER)),
                      wk_lds_bytes(PER, CPW), a.stream, static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N,
                      static_cast<const f16_t*>(a.pre), static_cast<const ST*>(a.post), static_cast<YT*>(a.Y));
   return hipGetLastError();
@@ -628,7 +652,8 @@ hipError_t launch_wk_rows(const LinearArgs& a) {
   const int per = wk_per(a.M);
   if (per == 1) return launch_wk<ST, YT, CPW, 1>(a);
   if (per == 2) return launch_wk<ST, YT, CPW, 2>(a);
-  return launch_wk<ST, YT, CPW, 4>(a);
+  if (per == 4) return launch_wk<ST, YT, CPW, 4>(a);
+  return launch_wk<ST, YT, CPW, 8>(a);
 }
 
 // Columns per wave of the whole-K variant, or 0 for the split kernel.
@@ -714,6 +739,7 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
       if (cpw > 0) return launch_wk_any<ST, YT>(a, cpw);
     }
   }
+  if (a.M > kDecodeMaxM) return hipErrorInvalidValue;   // the split kernel stages 16 rows
   if (b1) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
   if (b2) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);
   if (a.x_dtype == DT_BF16)
@@ -730,8 +756,26 @@ hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev) {
-  if (a.M < 1 || a.M > kDecodeMaxM) return hipErrorInvalidValue;
+  if (a.M < 1 || a.M > kDecodeWideMaxM || (a.M > kDecodeMaxM && !decode_wide_ok(a))) return hipErrorInvalidValue;
   return a.scale_dtype == DT_F32 ? launch_y<float>(a, dev) : launch_y<f16_t>(a, dev);
+}
+
+// 17..32 rows by default: on the whole-K kernel (one launch, fp32
+// contraction) while each of its 4 waves has at most 4 slices; the prefill
+// GEMM otherwise.  Same-box timings, us per call, GEMM vs whole-K: K = 4096
+// and N = 4096 11.3 / 8.3 (M = 17) and 12.7 / 8.4 (M = 32); N = 11008
+// 22.1 / 13.6 and 23.3 / 14.1; N = 14336 22.8 / 13.7 and 24.0 / 14.3; K = 11008,
+// N = 4096, M = 32 20.1 / 19.4; K = 14336, N = 4096, M = 24 22.6 / 23.0.
+bool decode_wide_preferred(const LinearArgs& a) {
+  return a.M > kDecodeMaxM && a.K <= 8192 && decode_wide_ok(a);
+}
+
+bool decode_wide_ok(const LinearArgs& a) {
+  const bool b2 = a.x_dtype == DT_BF16 && a.pre && a.scale_dtype == DT_F16;
+  const char* e = std::getenv("OBL_DECODE");
+  // (Y2, the bf16 copy of the output for a DBF prefill stage, is written by
+  // the prefill GEMM only.)
+  return a.M >= 1 && a.M <= kDecodeWideMaxM && !a.Y2 && wk_eligible(a, b2) && !(e && !std::strcmp(e, "split"));
 }
 
 }  // namespace obl

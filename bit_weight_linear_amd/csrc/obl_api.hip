@@ -89,7 +89,7 @@ Path choose_path(int64_t M, obl_status* st) {
     if (M <= kDecodeMaxM) return P_DECODE;
     return P_GEMM;
   }
-  if ((p == P_LUT && M > kLutMaxM) || (p == P_DECODE && M > kDecodeMaxM)) *st = OBL_ERR_SHAPE;
+  if ((p == P_LUT && M > kLutMaxM) || (p == P_DECODE && M > kDecodeWideMaxM)) *st = OBL_ERR_SHAPE;
   return p;
 }
 
@@ -98,6 +98,11 @@ std::unordered_map<int, DeviceInfo> g_info;
 std::unordered_map<int, Scratch> g_scratch;
 
 obl_status run_linear(const LinearArgs& la, Path path) {
+  // 17..32 rows: the decode path's whole-K kernel where it takes the call and
+  // is the faster choice (fp32 contraction, one launch); otherwise the
+  // prefill GEMM.  A forced decode call it cannot take is refused.
+  if (path == P_DECODE && la.M > kDecodeMaxM && !decode_wide_ok(la)) return OBL_ERR_SHAPE;
+  if (path == P_GEMM && forced_path() == P_AUTO && decode_wide_preferred(la)) path = P_DECODE;
   DeviceInfo dev;
   if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
   hipError_t e;

@@ -52,6 +52,11 @@ hipError_t launch_backward_grads(int x_dtype, int scale_dtype, int dx_dtype, con
 hipError_t launch_layernorm_rows(const void* Y, int y_dtype, int64_t M, int64_t N, float eps, const void* gamma,
                                  const void* beta, int g_dtype, void* Z, int z_dtype, hipStream_t st);
 hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
+// The decode path's whole-K kernel takes this call (bf16 x, fp16 scales,
+// aligned operands, K % 128 == 0, M <= kDecodeWideMaxM; not forced off).
+bool decode_wide_ok(const LinearArgs& a);
+// ... and is the faster choice for 17..32 rows (the automatic path).
+bool decode_wide_preferred(const LinearArgs& a);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
 // Main prefill kernel (bf16 activations); launch_gemm_mfma dispatches to it.
 bool gemm_wide_eligible(const LinearArgs& a);
@@ -64,8 +69,10 @@ hipError_t launch_gemm_wide(const LinearArgs& a, const DeviceInfo& dev);
 bool gemm_wide_prescale_eligible(const LinearArgs& a);
 hipError_t launch_gemm_wide_prescaled(const LinearArgs& a, const DeviceInfo& dev);
 
-// Largest M served by the LUT GEMV and by the decode kernel.
+// Largest M served by the LUT GEMV and by the decode kernels (the split
+// kernel: 16; the whole-K kernel: 32).
 constexpr int64_t kLutMaxM = 2;
 constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kDecodeWideMaxM = 32;
 
 }  // namespace obl

@@ -110,6 +110,9 @@ obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_
  *   final cast); for M > 16 (prefill) the contraction runs on bf16 matrix
  *   cores with one bf16 rounding of the input-side operand and fp32
  *   accumulation (<= 8e-3 on the same scale, including a bf16 output cast).
+ *   Calls of 17..32 rows with bf16 X, fp16 scales, 16-byte aligned X, packed
+ *   words and b and K % 128 == 0 run the decode path (fp32 accuracy) where it
+ *   is the faster choice (K <= 8192).
  *   Errors: OBL_ERR_NULL, OBL_ERR_SHAPE, OBL_ERR_DTYPE, OBL_ERR_ALIGN,
  *           OBL_ERR_ALIAS, OBL_ERR_HIP.
  */

@@ -90,7 +90,11 @@ def test_forced_path_must_fit_m(monkeypatch):
     monkeypatch.setenv("OBL_PATH", "lut")
     assert lin(M=3) == b.OBL_ERR_SHAPE
     monkeypatch.setenv("OBL_PATH", "decode")
-    assert lin(M=17) == b.OBL_ERR_SHAPE
+    assert lin(M=33) == b.OBL_ERR_SHAPE
+    # 17..32 rows only on the whole-K kernel (bf16 x, fp16 scales, aligned):
+    # fp32 x, or a K that is not a multiple of 128, is refused before any GPU work
+    assert lin(M=17, xd=b.OBL_F32) == b.OBL_ERR_SHAPE
+    assert lin(M=17, K=96) == b.OBL_ERR_SHAPE
     assert lin(M=0) == b.OBL_OK
 
 

@@ -1,5 +1,5 @@
-"""Decode path (3 <= M <= 16): the whole-K kernel against the fp64 oracle, and
-against the split-K kernel.
+"""Decode path (3 <= M <= 32): the whole-K kernel against the fp64 oracle, and
+against the split-K kernel (M <= 16).
 
 The whole-K kernel serves bf16 x with fp16 b, 16-byte aligned X and packed
 words, K % 128 == 0: one workgroup of 8 waves owns 16·CPW columns over all of
@@ -22,9 +22,12 @@ pytestmark = pytest.mark.gpu
 # (M, K, N): one partial slice (K = 128); two slices, the second of 4 steps
 # (K = 640); N not a multiple of the column block; two and five slices per
 # wave (K = 8192, 20480); the batched-decode shape and its 14336-wide variant.
+# 17..32 rows (two 16-row fragments, 4 waves per workgroup): ragged fragment
+# (17, 20), two slices per wave at K = 4096, a partial last slice (K = 640).
 WK_CASES = [
     (3, 128, 17), (5, 640, 100), (9, 4096, 1000), (16, 8192, 129), (16, 20480, 300),
     (16, 4096, 4096), (16, 4096, 14336), (8, 4096, 3072), (16, 1024, 65),
+    (17, 4096, 1000), (20, 640, 100), (24, 8192, 129), (32, 4096, 4096), (32, 4096, 14336),
 ]
 IMPLS = ["wk1", "wk2", "wk4", "split", "auto"]
 
@@ -36,8 +39,32 @@ def test_decode_kernels_match_oracle(M, K, N, ydt, impl, monkeypatch):
     G.say(f"decode {impl} M={M} K={K} N={N} y={ydt}")
     monkeypatch.setenv("OBL_DECODE", impl)
     c = WL.onebit_case(M, K, N, "bf16", "f16", ydt, seed=M * 7 + K + N)
+    if impl == "split" and M > 16:
+        # the split kernel stages 16 rows: a forced decode call is refused
+        with pytest.raises(B.OblError) as e:
+            G.run_onebit(c, "decode")
+        assert e.value.status == B.OBL_ERR_SHAPE
+        return
     r = G.check_onebit(c, G.run_onebit(c, "decode"), "decode")
     G.say(f"  max normalised error {r:.3e}")
+
+
+@pytest.mark.parametrize("M", [17, 24, 32])
+def test_mid_rows_default_to_whole_k(M):
+    """17..32 rows with bf16 x, fp16 scales and aligned operands take the
+    whole-K decode kernel by default: the decode path's 1e-5 bound holds."""
+    c = WL.onebit_case(M, 4096, 1000, "bf16", "f16", "f32", seed=M)
+    G.check_onebit(c, G.run_onebit(c), "decode")
+
+
+def test_mid_rows_fp32_x_take_the_gemm():
+    """fp32 x at 24 rows is not a whole-K call: the prefill GEMM serves it
+    (its 8e-3 bound), and a forced decode call is refused."""
+    c = WL.onebit_case(24, 1024, 300, "f32", "f32", "f32", seed=4)
+    G.check_onebit(c, G.run_onebit(c), "gemm")
+    with pytest.raises(B.OblError) as e:
+        G.run_onebit(c, "decode")
+    assert e.value.status == B.OBL_ERR_SHAPE
 
 
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (7, 2048, 1000), (16, 640, 33)])
