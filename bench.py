@@ -383,7 +383,7 @@ def main():
         sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
                         "algorithmic_bytes": int(ab5), "ideal_us_hbm": round(ab5 / HBM_PEAK_GBS / 1e3, 4),
                         "hbm_frac": round(ab5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "bound": "latency (two stages, three launches: stage 2 on the fp32 T1 splits K)",
+                        "bound": "latency (two stages, one launch each: stage 2 reads the exact bf16 terms of T1)",
                         "check_vs_torch_fp32": float(f"{e5:.3e}"), "copies": R5,
                         "stages_per_call": 2}
         log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")

@@ -386,25 +386,43 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // contraction.  Only where the sign words do not fit in LDS next to the rows
 // of X (CPW = 4 with M > 8) are they loaded into registers, at that cost.
 constexpr size_t WK_LDS_MAX = 160 * 1024;
-__host__ __device__ constexpr int wk_waves(int per) { return per == 8 ? 4 : 8; }
+constexpr size_t WK_LDS_UNITS = WK_LDS_MAX / 16;
 
-// LDS of one wave, in 16-byte units: X as four k-quarters, each [4·PER rows]
-// [16 chunks] (PER = DMAs of 4 rows per quarter, a template constant so the
-// waits are immediates); 64 b_hi pair quads and 64 b_lo pair quads (the raw
-// fp16 b of the slice lands in the b_lo area first); then, when they fit, the
-// sign words as [CPW][quarter][16 columns].  After the contraction the area
-// holds the reduction table.
-__host__ __device__ constexpr size_t wk_wave_units_nosigns(int per) { return (size_t)per * 256 + 128; }
-__host__ __device__ constexpr bool wk_signs_in_lds(int per, int cpw) {
-  return (size_t)wk_waves(per) * (wk_wave_units_nosigns(per) + 64 * (size_t)cpw) * 16 <= WK_LDS_MAX;
+// Input modes: WK_B2, bf16 x with fp16 b (mode B2 above); WK_T3, three bf16
+// arrays [3][M][K] whose sum is an fp32 input exactly (hi + mid + lo, written
+// by a previous whole-K call as its output's terms), no b: A = each term,
+// B = ±1, three MFMAs per step.  A DBF decode runs stage 1 in WK_B2 writing
+// the terms of T1 and stage 2 in WK_T3 reading them, each in one launch.
+enum WkMode { WK_B2 = 0, WK_T3 = 1 };
+
+// LDS of one wave, in 16-byte units: X as TT term arrays (TT = 1, or 3 for
+// WK_T3), each four k-quarters of [4·PER rows][16 chunks] (PER = DMAs of 4
+// rows per quarter, a template constant so the waits are immediates); WK_B2:
+// 64 b_hi pair quads and 64 b_lo pair quads (the raw fp16 b of the slice
+// lands in the b_lo area first); then, when they fit, the sign words as
+// [CPW][quarter][16 columns].  After the contraction the area holds the
+// reduction table.  Waves per workgroup: 8, or 4 for 17..32 rows (WK_B2);
+// WK_T3 as many as fit, at most 8 (6 for 8 rows).
+__host__ __device__ constexpr size_t wk_wave_units_nosigns(int xm, int per) {
+  return xm == WK_T3 ? (size_t)per * 768 : (size_t)per * 256 + 128;
 }
-__host__ __device__ constexpr size_t wk_wave_units(int per, int cpw) {
-  return wk_wave_units_nosigns(per) + (wk_signs_in_lds(per, cpw) ? 64 * (size_t)cpw : 0);
+__host__ __device__ constexpr int wk_waves(int xm, int per, int cpw) {
+  return xm == WK_B2 ? (per == 8 ? 4 : 8)
+                     : (int)(WK_LDS_UNITS / (wk_wave_units_nosigns(xm, per) + 64 * (size_t)cpw) < 8
+                                 ? WK_LDS_UNITS / (wk_wave_units_nosigns(xm, per) + 64 * (size_t)cpw)
+                                 : 8);
+}
+__host__ __device__ constexpr bool wk_signs_in_lds(int xm, int per, int cpw) {
+  return (size_t)wk_waves(xm, per, cpw) * (wk_wave_units_nosigns(xm, per) + 64 * (size_t)cpw) <= WK_LDS_UNITS;
+}
+__host__ __device__ constexpr size_t wk_wave_units(int xm, int per, int cpw) {
+  return wk_wave_units_nosigns(xm, per) + (wk_signs_in_lds(xm, per, cpw) ? 64 * (size_t)cpw : 0);
 }
 inline int wk_per(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : (M <= 16 ? 4 : 8)); }
-inline size_t wk_lds_bytes(int per, int cpw) {
-  const size_t stage = (size_t)wk_waves(per) * wk_wave_units(per, cpw) * 16;
-  const size_t red = (size_t)wk_waves(per) * 4 * per * (16 * cpw + 1) * sizeof(float);
+inline size_t wk_lds_bytes(int xm, int per, int cpw) {
+  const size_t waves = (size_t)wk_waves(xm, per, cpw);
+  const size_t stage = waves * wk_wave_units(xm, per, cpw) * 16;
+  const size_t red = waves * 4 * per * (16 * cpw + 1) * sizeof(float);
   return stage > red ? stage : red;
 }
 
@@ -423,19 +441,24 @@ __device__ __forceinline__ void wk_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename ST, typename YT, int CPW, int PER>
-__global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
+// T3 (optional, fp32 Y only): the output's exact bf16 terms, [3][M][N].
+template <int XM, typename ST, typename YT, int CPW, int PER>
+__global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
-    const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y) {
-  constexpr int WAVES = wk_waves(PER);
+    const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3) {
+  constexpr bool B2 = XM == WK_B2;
+  constexpr int TT = B2 ? 1 : 3;                                  // A term arrays
+  constexpr int NA = B2 ? 2 : 3;                                  // accumulators per set
+  constexpr int WAVES = wk_waves(XM, PER, CPW);
   constexpr int THREADS = 64 * WAVES;
   constexpr int NC = 16 * CPW;                                    // columns per workgroup
   constexpr int RS = NC + 1;                                      // reduction table row stride (floats)
   constexpr int M4 = 4 * PER;                                     // X rows staged (>= M)
+  constexpr int TS = 4 * M4 * 16;                                 // units per term array
   constexpr int RF = (M4 + 15) / 16;                              // 16-row fragments
   constexpr int NOUT = (16 * RF * NC + THREADS - 1) / THREADS;    // final outputs per thread
-  constexpr bool SL = wk_signs_in_lds(PER, CPW);                  // sign words by DMA into LDS
-  constexpr int NSIG = SL ? CPW : 0;                              // sign DMAs per slice
+  constexpr bool SL = wk_signs_in_lds(XM, PER, CPW);              // sign words by DMA into LDS
+  constexpr int XD = TT * PER;                                    // X DMAs per k-quarter
   extern __shared__ u32x4 wk_lds[];
 
   const int tid = threadIdx.x;
@@ -446,16 +469,16 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
   const int64_t kw = K >> 5;
   const int nslices = (int)((kw + DEC_STEPS - 1) / DEC_STEPS);
   const int64_t n0 = (int64_t)blockIdx.x * NC;
-  u32x4* xw = wk_lds + (size_t)wave * wk_wave_units(PER, CPW);   // X quarters
-  u32x4* mq = xw + M4 * 64;                                       // b_hi quads [64], b_lo quads [64]
+  u32x4* xw = wk_lds + (size_t)wave * wk_wave_units(XM, PER, CPW);   // X terms and quarters
+  u32x4* mq = xw + TT * TS;                                       // WK_B2: b_hi quads [64], b_lo quads [64]
   uint32_t* mw = reinterpret_cast<uint32_t*>(mq);
-  u32x4* sg = mq + 128;                                           // sign quads [CPW][4][16] (SL)
+  u32x4* sg = mq + (B2 ? 128 : 0);                                // sign quads [CPW][4][16] (SL)
   // Buffer resources: offsets past the end of X, W or b read zeros, so the
   // DMAs need no clamping (what they read past the last slice's K is masked).
   // Byte offsets fit in 32 bits (checked by the launcher).
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(TT * M * K * 2));
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)(N * kw * 4));
-  const __amdgpu_buffer_rsrc_t br = make_rsrc(pre, (uint32_t)(K * 2));
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(B2 ? (const void*)pre : (const void*)W, B2 ? (uint32_t)(K * 2) : 0u);
   // Per-lane DMA offsets, fixed over the slices: X row group i (row 4i +
   // lane / 16, chunk (lane % 16) ^ (row % 16) of a quarter), sign quad lane / 16
   // of column 16c + lane % 16, b chunk lane.
@@ -484,6 +507,7 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
   }
   const int h = g >> 1;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   bool mrow[RF];                                                  // row 16f + j of fragment f exists
   int xrow[RF];
 #pragma unroll
@@ -498,13 +522,15 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
   // with more, the column groups already give the MFMAs enough independent
   // chains and fewer sets keep the registers within two waves per SIMD.
   constexpr int AU = CPW == 1 ? 4 : (CPW == 2 ? 2 : 1);
-  f32x4 acc[AU][CPW][RF][2];
+  f32x4 acc[AU][CPW][RF][NA];
 #pragma unroll
   for (int u = 0; u < AU; ++u)
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int f = 0; f < RF; ++f) acc[u][c][f][0] = acc[u][c][f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int a = 0; a < NA; ++a) acc[u][c][f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int s = wave; s < nslices; s += WAVES) {
     const int64_t step0 = (int64_t)s * DEC_STEPS;
@@ -529,24 +555,27 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
     // The waits below count transfers in issue order: scheduling barriers
     // keep the compiler from reordering the groups.
     __builtin_amdgcn_sched_barrier(0);
-    // b of the slice, raw fp16, lane l -> k0 + 8l .. +7 into the b_lo area
-    // (chunks past K re-read chunk 0; masked when converted).
-    dma16(br, mq + 64, (uint32_t)(16 * lane), (uint32_t)(k0 * 2));
+    // WK_B2: b of the slice, raw fp16, lane l -> k0 + 8l .. +7 into the b_lo
+    // area (chunks past K read zeros or the next values; masked when converted).
+    if constexpr (B2) dma16(br, mq + 64, (uint32_t)(16 * lane), (uint32_t)(k0 * 2));
     __builtin_amdgcn_sched_barrier(0);
-    // X quarter q (k0 + 128q .. +127): DMA i writes rows 4i .. 4i+3, lane l ->
-    // row 4i + l/16, slot l % 16 = chunk (l % 16) ^ (row % 16) of the quarter.
-    // Rows past M re-read row M - 1 (never used).
+    // X quarter q (k0 + 128q .. +127) of term array tt: DMA i writes rows 4i ..
+    // 4i+3, lane l -> row 4i + l/16, slot l % 16 = chunk (l % 16) ^ (row % 16)
+    // of the quarter.  Rows past M re-read row M - 1 (never used).
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) dma16(xr, xw + (q * M4 + 4 * i) * 16, xo[i], (uint32_t)((k0 + 128 * q) * 2));
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          dma16(xr, xw + tt * TS + (q * M4 + 4 * i) * 16, xo[i], (uint32_t)((tt * M * K + k0 + 128 * q) * 2));
       __builtin_amdgcn_sched_barrier(0);
     }
-    wk_wait_vm<3 * PER>();   // signs, b and quarter 0 landed
+    wk_wait_vm<3 * XD>();   // signs, b and quarter 0 landed
     wk_wave_sync();
-    // b pairs -> (b_hi, b_lo) tables: dword p = lane + 64 i holds k0 + 2p and
-    // k0 + 2p + 1; every lane reads its four raw dwords before writing.
-    {
+    if constexpr (B2) {
+      // b pairs -> (b_hi, b_lo) tables: dword p = lane + 64 i holds k0 + 2p and
+      // k0 + 2p + 1; every lane reads its four raw dwords before writing.
       uint32_t raw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[i] = mw[256 + lane + 64 * i];
@@ -560,42 +589,56 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
         mw[p] = pack_bf16_pair(h0, h1);
         mw[256 + p] = pack_bf16_pair(b0 - h0, b1 - h1);   // exact (fp16 residual)
       }
+      wk_wave_sync();
     }
-    wk_wave_sync();
 
 #pragma unroll
     for (int t = 0; t < DEC_STEPS; t += 4) {
       // Quarter t / 4: wait for its DMAs (the later quarters may still fly).
-      if (t == 4) wk_wait_vm<2 * PER>();
-      if (t == 8) wk_wait_vm<PER>();
+      if (t == 4) wk_wait_vm<2 * XD>();
+      if (t == 8) wk_wait_vm<XD>();
       if (t == 12) wk_wait_vm<0>();
       if (t > 0) wk_wave_sync();
-      u32x4 xf[4][RF], mh[4], ml[4], wv[CPW];
+      u32x4 xf[4][RF][TT], mh[4], ml[4], wv[CPW];
 #pragma unroll
       for (int c = 0; c < CPW; ++c) wv[c] = SL ? sg[(4 * c + t / 4) * 16 + j] : wq[SL ? 0 : c][t / 4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int kb = 32 * (t + u) + 8 * g;
 #pragma unroll
-        for (int f = 0; f < RF; ++f) xf[u][f] = xw[(t / 4) * M4 * 16 + xrow[f] + ((4 * u + g) ^ swz)];
-        mh[u] = mq[kb / 8];
-        ml[u] = mq[64 + kb / 8];
+        for (int f = 0; f < RF; ++f)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) xf[u][f][tt] = xw[tt * TS + (t / 4) * M4 * 16 + xrow[f] + ((4 * u + g) ^ swz)];
+        if constexpr (B2) {
+          mh[u] = mq[kb / 8];
+          ml[u] = mq[64 + kb / 8];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);   // every LDS read of the quarter before its first MFMA
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        u32x4 a[RF];
-#pragma unroll
-        for (int f = 0; f < RF; ++f) a[f] = (mrow[f] && (t + u < nsteps)) ? xf[u][f] : zero4;
+        const bool live = t + u < nsteps;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
           const uint32_t word = wv[c][u];
-          const u32x4 bh = expand_nat(word, h, sh, mh[u]), bl = expand_nat(word, h, sh, ml[u]);
+          if constexpr (B2) {
+            const u32x4 bh = expand_nat(word, h, sh, mh[u]), bl = expand_nat(word, h, sh, ml[u]);
 #pragma unroll
-          for (int f = 0; f < RF; ++f) {
-            f32x4* ac = acc[u % AU][c][f];
-            ac[0] = mfma16x16x32(a[f], bh, ac[0]);
-            ac[1] = mfma16x16x32(a[f], bl, ac[1]);
+            for (int f = 0; f < RF; ++f) {
+              const u32x4 a = (mrow[f] && live) ? xf[u][f][0] : zero4;
+              f32x4* ac = acc[u % AU][c][f];
+              ac[0] = mfma16x16x32(a, bh, ac[0]);
+              ac[1] = mfma16x16x32(a, bl, ac[1]);
+            }
+          } else {
+            const u32x4 bs = expand_nat(word, h, sh, ones);
+#pragma unroll
+            for (int f = 0; f < RF; ++f) {
+              f32x4* ac = acc[u % AU][c][f];
+#pragma unroll
+              for (int tt = 0; tt < TT; ++tt)
+                ac[tt] = mfma16x16x32((mrow[f] && live) ? xf[u][f][tt] : zero4, bs, ac[tt]);
+            }
           }
         }
       }
@@ -611,7 +654,12 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
     for (int f = 0; f < RF; ++f) {
       tot[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < AU; ++u) tot[c][f] = tot[c][f] + (acc[u][c][f][0] + acc[u][c][f][1]);
+      for (int u = 0; u < AU; ++u) {
+        f32x4 su = acc[u][c][f][0];
+#pragma unroll
+        for (int a = 1; a < NA; ++a) su = su + acc[u][c][f][a];
+        tot[c][f] = tot[c][f] + su;
+      }
     }
   // Waves' sums through LDS: red[wave][row][column]; lane holds rows
   // 16f + 4g .. +3 of column 16c + j.  Added in wave order.
@@ -632,28 +680,41 @@ __global__ __launch_bounds__(64 * wk_waves(PER)) void decode_wk_kernel(
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) v += red[(w * 16 * RF + m) * RS + cl];
-      Store<YT>::put(&Y[(int64_t)m * N + n0 + cl], v * post_o[r]);
+      const float y = v * post_o[r];
+      const int64_t e = (int64_t)m * N + n0 + cl;
+      Store<YT>::put(&Y[e], y);
+      if (T3) {
+        // Exact terms of the fp32 output for a following WK_T3 call.
+        const Split3 sp = split3(y);
+        Store<bf16_t>::put(&T3[e], sp.hi);
+        Store<bf16_t>::put(&T3[(int64_t)M * N + e], sp.mid);
+        Store<bf16_t>::put(&T3[2 * (int64_t)M * N + e], sp.lo);
+      }
     }
   }
 }
 
-template <typename ST, typename YT, int CPW, int PER>
+template <int XM, typename ST, typename YT, int CPW, int PER>
 hipError_t launch_wk(const LinearArgs& a) {
   const int64_t blocks = (a.N + 16 * CPW - 1) / (16 * CPW);
   if (blocks > 0x7fffffff || a.M > 4 * PER) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_wk_kernel<ST, YT, CPW, PER>), dim3((unsigned)blocks), dim3(64 * wk_waves(PER)),
-                     wk_lds_bytes(PER, CPW), a.stream, static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N,
-                     static_cast<const f16_t*>(a.pre), static_cast<const ST*>(a.post), static_cast<YT*>(a.Y));
+  hipLaunchKernelGGL((decode_wk_kernel<XM, ST, YT, CPW, PER>), dim3((unsigned)blocks),
+                     dim3(64 * wk_waves(XM, PER, CPW)), wk_lds_bytes(XM, PER, CPW), a.stream,
+                     static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N, static_cast<const f16_t*>(a.pre),
+                     static_cast<const ST*>(a.post), static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.T3));
   return hipGetLastError();
 }
 
-template <typename ST, typename YT, int CPW>
+template <int XM, typename ST, typename YT, int CPW>
 hipError_t launch_wk_rows(const LinearArgs& a) {
   const int per = wk_per(a.M);
-  if (per == 1) return launch_wk<ST, YT, CPW, 1>(a);
-  if (per == 2) return launch_wk<ST, YT, CPW, 2>(a);
-  if (per == 4) return launch_wk<ST, YT, CPW, 4>(a);
-  return launch_wk<ST, YT, CPW, 8>(a);
+  if (per == 1) return launch_wk<XM, ST, YT, CPW, 1>(a);
+  if (per == 2) return launch_wk<XM, ST, YT, CPW, 2>(a);
+  if constexpr (XM == WK_B2) {
+    if (per == 4) return launch_wk<XM, ST, YT, CPW, 4>(a);
+    return launch_wk<XM, ST, YT, CPW, 8>(a);
+  }
+  return hipErrorInvalidValue;   // WK_T3 serves up to 8 rows
 }
 
 // Columns per wave of the whole-K variant, or 0 for the split kernel.
@@ -676,20 +737,24 @@ int wk_columns_per_wave(const LinearArgs& a, const DeviceInfo& dev) {
   return cpw;
 }
 
-// Mode B2 with every operand the kernel DMAs 16-byte aligned.
-bool wk_eligible(const LinearArgs& a, bool b2) {
-  // Buffer byte ranges (and offsets, with one slice to spare) within 32 bits.
+// Operands the kernel DMAs 16-byte aligned, K % 128 == 0, byte ranges (and
+// offsets, with one slice to spare) within 32 bits.  `terms`: X is [3][M][K].
+bool wk_operands_ok(const LinearArgs& a, int terms) {
   const int64_t lim = (int64_t)0xFFFFF000u - 4096;
-  return b2 && a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
-         reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && reinterpret_cast<uintptr_t>(a.pre) % 16 == 0 &&
-         a.M * a.K * 2 <= lim && a.N * (a.K / 32) * 4 <= lim;
+  return a.K % 128 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.W) % 16 == 0 && terms * a.M * a.K * 2 <= lim && a.N * (a.K / 32) * 4 <= lim;
 }
 
-template <typename ST, typename YT>
+// Mode B2 with b 16-byte aligned too.
+bool wk_eligible(const LinearArgs& a, bool b2) {
+  return b2 && reinterpret_cast<uintptr_t>(a.pre) % 16 == 0 && wk_operands_ok(a, 1);
+}
+
+template <int XM, typename ST, typename YT>
 hipError_t launch_wk_any(const LinearArgs& a, int cpw) {
-  if (cpw == 4) return launch_wk_rows<ST, YT, 4>(a);
-  if (cpw == 2) return launch_wk_rows<ST, YT, 2>(a);
-  return launch_wk_rows<ST, YT, 1>(a);
+  if (cpw == 4) return launch_wk_rows<XM, ST, YT, 4>(a);
+  if (cpw == 2) return launch_wk_rows<XM, ST, YT, 2>(a);
+  return launch_wk_rows<XM, ST, YT, 1>(a);
 }
 
 template <int MODE, typename XT, typename ST, typename YT, bool PRE>
@@ -733,12 +798,19 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
   const bool b1 = raw && !a.pre, b2 = raw && a.pre && a.scale_dtype == DT_F16;
   // (Every public entry point passes an input-side scale, so only mode B2
   // reaches the whole-K variant.)
+  if (a.x_dtype == DT_BF16X3) {
+    // Exact bf16 terms of an fp32 input (DBF stage 2): the whole-K kernel only.
+    const int cpw = wk_columns_per_wave(a, dev);
+    if (a.pre || a.T3 || a.M > 8 || cpw == 0 || !wk_operands_ok(a, 3)) return hipErrorInvalidValue;
+    return launch_wk_any<WK_T3, ST, YT>(a, cpw);
+  }
   if constexpr (std::is_same<ST, f16_t>::value) {
     if (wk_eligible(a, b2)) {
       const int cpw = wk_columns_per_wave(a, dev);
-      if (cpw > 0) return launch_wk_any<ST, YT>(a, cpw);
+      if (cpw > 0 && (!a.T3 || std::is_same<YT, float>::value)) return launch_wk_any<WK_B2, ST, YT>(a, cpw);
     }
   }
+  if (a.T3) return hipErrorInvalidValue;                // only the whole-K kernel writes the terms
   if (a.M > kDecodeMaxM) return hipErrorInvalidValue;   // the split kernel stages 16 rows
   if (b1) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
   if (b2) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);
@@ -768,6 +840,13 @@ hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev) {
 // N = 4096, M = 32 20.1 / 19.4; K = 14336, N = 4096, M = 24 22.6 / 23.0.
 bool decode_wide_preferred(const LinearArgs& a) {
   return a.M > kDecodeMaxM && a.K <= 8192 && decode_wide_ok(a);
+}
+
+bool decode_terms_ok(const LinearArgs& s1, const LinearArgs& s2) {
+  if (!decode_wide_ok(s1) || s1.M > 8 || s1.y_dtype != DT_F32 || s2.pre) return false;
+  LinearArgs t = s2;
+  t.X = s2.W;   // the terms go to 256-byte aligned library scratch: only sizes and W are checked
+  return wk_operands_ok(t, 3);
 }
 
 bool decode_wide_ok(const LinearArgs& a) {

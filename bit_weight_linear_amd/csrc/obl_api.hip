@@ -514,6 +514,20 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
         s2.x_dtype = OBL_BF16;
       }
     }
+    // Decode (up to 8 rows): stage 1 on the whole-K kernel also writes the
+    // exact bf16 terms of T1 (hi + mid + lo) into library scratch, and stage 2
+    // reads those terms on the same kernel: one launch per stage, and the
+    // products stay exact.
+    if (path == P_DECODE && decode_terms_ok(s1, s2)) {
+      DeviceInfo dev;
+      if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+      Scratch sc{};
+      const size_t floats = (size_t)((3 * M * Kmid + 1) / 2 + 64);
+      if (scratch_reserve(dev.device, floats, &sc) != hipSuccess) return OBL_ERR_HIP;
+      s1.T3 = sc.partials;
+      s2.X = sc.partials;
+      s2.x_dtype = DT_BF16X3;
+    }
     st = run_linear(s1, path);
     if (st != OBL_OK) return st;
     return run_linear(s2, path);

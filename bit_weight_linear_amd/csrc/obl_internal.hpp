@@ -6,10 +6,15 @@
 
 namespace obl {
 
+// Internal x_dtype: three bf16 arrays [3][rows][cols] whose sum hi + mid + lo
+// is an fp32 value exactly (public dtype codes stay below 16).
+constexpr int kDtBf16x3 = 16;
+constexpr int DT_BF16X3 = kDtBf16x3;
+
 // One sign-binarised contraction Y = ((X ⊙ pre) · W^T) ⊙ post.
 struct LinearArgs {
   const void* X;      // [M][K], x_dtype
-  int x_dtype;        // DT_F32 or DT_BF16
+  int x_dtype;        // DT_F32 or DT_BF16 (internally also DT_BF16X3: DBF stage 2 on the decode path)
   int64_t M, K;
   const uint32_t* W;  // [N][K/32] packed signs
   int64_t N;
@@ -20,6 +25,7 @@ struct LinearArgs {
   int y_dtype;        // DT_F32 or DT_BF16
   hipStream_t stream;
   void* Y2 = nullptr; // optional bf16 copy of Y (prefill GEMM only; see gemm_wide_eligible)
+  void* T3 = nullptr; // optional exact bf16 terms of an fp32 Y, [3][M][N] (decode whole-K kernel only)
 };
 
 struct DeviceInfo {
@@ -57,6 +63,9 @@ hipError_t launch_decode_mfma(const LinearArgs& a, const DeviceInfo& dev);
 bool decode_wide_ok(const LinearArgs& a);
 // ... and is the faster choice for 17..32 rows (the automatic path).
 bool decode_wide_preferred(const LinearArgs& a);
+// A DBF decode can run both stages on the whole-K kernel: stage 1 writes the
+// exact bf16 terms of T1 (s1.T3), stage 2 reads them (x_dtype DT_BF16X3).
+bool decode_terms_ok(const LinearArgs& s1, const LinearArgs& s2);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
 // Main prefill kernel (bf16 activations); launch_gemm_mfma dispatches to it.
 bool gemm_wide_eligible(const LinearArgs& a);

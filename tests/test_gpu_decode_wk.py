@@ -132,3 +132,45 @@ def test_dbf_decode_stage1_whole_k(impl, monkeypatch):
                                O.dbf_error_scale(c.X, c.b, c.m, c.a))
     G.say(f"dbf {impl}: stage1 {r1:.3e} composed {r:.3e}")
     assert r1 <= G.TOL_DECODE and r <= G.TOL_DECODE
+
+
+@pytest.mark.parametrize("impl", ["auto", "wk1", "wk2", "wk4"])
+@pytest.mark.parametrize("M,K,Kmid,N", [(8, 4096, 3072, 4096), (3, 1024, 640, 300), (5, 4096, 4096, 1000),
+                                        (8, 512, 128, 4096)])
+def test_dbf_decode_through_exact_terms(M, K, Kmid, N, impl, monkeypatch):
+    """Up to 8 rows with both stages on the whole-K kernel: stage 1 writes the
+    exact bf16 terms (hi + mid + lo) of T1 and stage 2 contracts them against
+    the signs of S1.  T1 is bitwise the single-stage result; both stages meet
+    the decode tolerance against the oracle."""
+    if impl != "auto":
+        monkeypatch.setenv("OBL_DECODE", impl)
+    G.say(f"dbf terms {impl} M={M} K={K} Kmid={Kmid} N={N}")
+    c = WL.dbf_case(M, K, Kmid, N, seed=K + Kmid + N + M)
+    X = G.dev(c.X, "bf16")
+    S2p = B.pack_signs(G.signs_dev(c.S2))
+    S1p = B.pack_signs(G.signs_dev(c.S1))
+    b, m, a = (G.dev(v, "f16") for v in (c.b, c.m, c.a))
+    Y, T1 = B.dbf_linear(X, S2p, S1p, b, m, a)
+    T1b = B.linear(X, S2p, m, b)
+    assert torch.equal(T1, T1b)
+    Th = G.host64(T1)
+    r1 = O.max_normalised_error(Th, O.dbf_stage1(c.X, c.S2, c.b, c.m), O.onebit_error_scale(c.X, c.m, c.b))
+    # stage 2 against the oracle applied to the device's T1 (the terms carry T1 exactly)
+    r2 = O.max_normalised_error(G.host64(Y), O.onebit_linear(Th, c.S1, c.a, np.ones(Kmid)),
+                                O.onebit_error_scale(Th, c.a, np.ones(Kmid)))
+    r = O.max_normalised_error(G.host64(Y), O.dbf_linear(c.X, c.S1, c.S2, c.a, c.m, c.b),
+                               O.dbf_error_scale(c.X, c.b, c.m, c.a))
+    G.say(f"  stage1 {r1:.3e} stage2 {r2:.3e} composed {r:.3e}")
+    assert r1 <= G.TOL_DECODE and r2 <= G.TOL_DECODE and r <= G.TOL_DECODE
+
+
+def test_dbf_decode_terms_integer_exact():
+    """Integer-valued DBF at 8 rows through the exact terms: bit-exact."""
+    c = WL.dbf_case(8, 4096, 3072, 4096, kind="int_exact", seed=8)
+    X = G.dev(c.X, "bf16")
+    S2p = B.pack_signs(G.signs_dev(c.S2))
+    S1p = B.pack_signs(G.signs_dev(c.S1))
+    b, m, a = (G.dev(v, "f16") for v in (c.b, c.m, c.a))
+    Y, T1 = B.dbf_linear(X, S2p, S1p, b, m, a)
+    assert np.array_equal(G.host64(T1), O.dbf_stage1(c.X, c.S2, c.b, c.m))
+    assert np.array_equal(G.host64(Y), O.dbf_linear(c.X, c.S1, c.S2, c.a, c.m, c.b))
