@@ -422,7 +422,8 @@ inline int wk_per(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : (M <= 16 ? 4 : 
 inline size_t wk_lds_bytes(int xm, int per, int cpw) {
   const size_t waves = (size_t)wk_waves(xm, per, cpw);
   const size_t stage = waves * wk_wave_units(xm, per, cpw) * 16;
-  const size_t red = waves * 4 * per * (16 * cpw + 1) * sizeof(float);
+  const size_t rows = (size_t)(4 * per + 15) / 16 * 16;
+  const size_t red = (waves * rows * (16 * cpw + 1) + rows * 16 * cpw) * sizeof(float);   // + gradient products
   return stage > red ? stage : red;
 }
 
@@ -441,11 +442,17 @@ __device__ __forceinline__ void wk_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// T3 (optional, fp32 Y only): the output's exact bf16 terms, [3][M][N].
+// Optional epilogue outputs (null when unused).  T3 (fp32 Y only): the
+// output's exact bf16 terms, [3][M][N].  Gradient epilogue of the layer's
+// backward (bf16 gin): gsum[n] = Σ_m gin[m][n] · y[m][n] over the block's
+// rows in order, and, with gout, gout[m][n] = y[m][n] · gscale[n] (fp32 or
+// bf16 as gout_bf16 says).
 template <int XM, typename ST, typename YT, int CPW, int PER>
 __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
-    const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3) {
+    const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3,
+    const bf16_t* __restrict__ gin, float* __restrict__ gsum, const ST* __restrict__ gscale,
+    void* __restrict__ gout, int gout_bf16) {
   constexpr bool B2 = XM == WK_B2;
   constexpr int TT = B2 ? 1 : 3;                                  // A term arrays
   constexpr int NA = B2 ? 2 : 3;                                  // accumulators per set
@@ -498,6 +505,17 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
 #pragma unroll
   for (int r = 0; r < NOUT; ++r)
     post_o[r] = scale_or_one(post, min(n0 + (tid + THREADS * r) % NC, N - 1), W);   // W: >= 4N bytes
+  // Gradient epilogue inputs of the same outputs: unconditional loads
+  // (clamped indexes; without gin, element 0 of W stands in and is unused).
+  float gin_o[NOUT], gsc_o[NOUT];
+  const bf16_t* gsrc = gin ? gin : reinterpret_cast<const bf16_t*>(W);
+#pragma unroll
+  for (int r = 0; r < NOUT; ++r) {
+    const int o = tid + THREADS * r;
+    const int64_t mm = min(o / NC, M - 1), nn = min(n0 + o % NC, N - 1);
+    gin_o[r] = to_f32(gsrc[gin ? mm * N + nn : 0]);
+    gsc_o[r] = scale_or_one(gscale, nn, W);
+  }
 
   u16x2 sh[4];
 #pragma unroll
@@ -672,6 +690,7 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[(wave * 16 * RF + 16 * f + 4 * g + i) * RS + 16 * c + j] = tot[c][f][i];
   __syncthreads();
+  float* pg = red + WAVES * 16 * RF * RS;   // gradient products [16·RF rows][NC]
 #pragma unroll
   for (int r = 0; r < NOUT; ++r) {
     const int o = tid + THREADS * r;
@@ -690,6 +709,20 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
         Store<bf16_t>::put(&T3[(int64_t)M * N + e], sp.mid);
         Store<bf16_t>::put(&T3[2 * (int64_t)M * N + e], sp.lo);
       }
+      if (gsum) pg[m * NC + cl] = gin_o[r] * y;
+      if (gout) {
+        const float d = y * gsc_o[r];
+        if (gout_bf16) Store<bf16_t>::put(&static_cast<bf16_t*>(gout)[e], d);
+        else static_cast<float*>(gout)[e] = d;
+      }
+    }
+  }
+  if (gsum) {   // uniform: every thread takes the same branch
+    __syncthreads();
+    if (tid < NC && n0 + tid < N) {
+      float sum = 0.f;
+      for (int m = 0; m < M; ++m) sum += pg[m * NC + tid];
+      gsum[n0 + tid] = sum;
     }
   }
 }
@@ -701,7 +734,9 @@ hipError_t launch_wk(const LinearArgs& a) {
   hipLaunchKernelGGL((decode_wk_kernel<XM, ST, YT, CPW, PER>), dim3((unsigned)blocks),
                      dim3(64 * wk_waves(XM, PER, CPW)), wk_lds_bytes(XM, PER, CPW), a.stream,
                      static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N, static_cast<const f16_t*>(a.pre),
-                     static_cast<const ST*>(a.post), static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.T3));
+                     static_cast<const ST*>(a.post), static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.T3),
+                     static_cast<const bf16_t*>(a.gin), a.gsum, static_cast<const ST*>(a.gscale), a.gout,
+                     a.gout_dtype == DT_BF16 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -810,7 +845,7 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
       if (cpw > 0 && (!a.T3 || std::is_same<YT, float>::value)) return launch_wk_any<WK_B2, ST, YT>(a, cpw);
     }
   }
-  if (a.T3) return hipErrorInvalidValue;                // only the whole-K kernel writes the terms
+  if (a.T3 || a.gsum || a.gout) return hipErrorInvalidValue;   // epilogues of the whole-K kernel only
   if (a.M > kDecodeMaxM) return hipErrorInvalidValue;   // the split kernel stages 16 rows
   if (b1) return launch_t<MODE_B1, bf16_t, ST, YT, false>(a, dev);
   if (b2) return launch_t<MODE_B2, bf16_t, ST, YT, true>(a, dev);

@@ -376,9 +376,26 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
     float* U = workspace + M * N;         // [M][K]
     // T = (X ⊙ b^T) W_sign^T and U = (dY ⊙ a^T) W_sign, both without an output scale.
     LinearArgs t{X, x_dtype, M, K, W_packed, N, b, nullptr, scale_dtype, T, OBL_F32, hs};
+    LinearArgs u{dY, x_dtype, M, N, Wt_packed, K, a, nullptr, scale_dtype, U, OBL_F32, hs};
+    // Both contractions on the decode path's whole-K kernel: its epilogue
+    // forms the gradients (da from T and dY; dX and db from U, b and X), so no
+    // separate reduction launch.
+    const bool auto_wide = path == P_GEMM && forced_path() == P_AUTO && decode_wide_preferred(t) &&
+                           decode_wide_preferred(u);
+    if ((path == P_DECODE || auto_wide) && decode_wide_ok(t) && decode_wide_ok(u)) {
+      t.gin = dY;
+      t.gsum = da;
+      u.gin = X;
+      u.gsum = db;
+      u.gscale = b;
+      u.gout = dX;
+      u.gout_dtype = dx_dtype;
+      st = run_linear(t, path);
+      if (st != OBL_OK) return st;
+      return run_linear(u, path);
+    }
     st = run_linear(t, path);
     if (st != OBL_OK) return st;
-    LinearArgs u{dY, x_dtype, M, N, Wt_packed, K, a, nullptr, scale_dtype, U, OBL_F32, hs};
     st = run_linear(u, path);
     if (st != OBL_OK) return st;
     hipError_t e = launch_backward_grads(x_dtype, scale_dtype, dx_dtype, dY, X, T, U, b, M, K, N, dX, da,

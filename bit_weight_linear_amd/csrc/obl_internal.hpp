@@ -26,6 +26,15 @@ struct LinearArgs {
   hipStream_t stream;
   void* Y2 = nullptr; // optional bf16 copy of Y (prefill GEMM only; see gemm_wide_eligible)
   void* T3 = nullptr; // optional exact bf16 terms of an fp32 Y, [3][M][N] (decode whole-K kernel only)
+  // Optional gradient epilogue (decode whole-K kernel only; the layer's
+  // backward): gsum[n] = Σ_m gin[m][n] · Y[m][n] (gin in x_dtype, gsum fp32),
+  // and gout[m][n] = Y[m][n] · gscale[n] (gscale in scale_dtype, gout in
+  // gout_dtype) when gout is set.
+  const void* gin = nullptr;
+  float* gsum = nullptr;
+  const void* gscale = nullptr;
+  void* gout = nullptr;
+  int gout_dtype = 0;
 };
 
 struct DeviceInfo {

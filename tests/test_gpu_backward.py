@@ -45,8 +45,12 @@ def _run(X, dY, S, a, b, x_dtype, scale_dtype, dx_dtype):
     return G.host64(dX), G.host64(da), G.host64(db), ws
 
 
+# (5, 1024, 512), (16, 4096, 4096), (17, 4096, 512) and (24, 1152, 640) with bf16
+# inputs run both contractions on the whole-K decode kernel, whose epilogue
+# forms dX, da and db; (9, 544, 96) and fp32 inputs take the reduction kernel.
 @pytest.mark.parametrize("M,K,N", [(1, 512, 256), (2, 4096, 1024), (5, 1024, 512), (16, 4096, 4096),
-                                   (9, 544, 96), (64, 1024, 1024), (300, 512, 768), (17, 4096, 512)])
+                                   (9, 544, 96), (64, 1024, 1024), (300, 512, 768), (17, 4096, 512),
+                                   (24, 1152, 640)])
 @pytest.mark.parametrize("dts", [("bf16", "f16", "f32"), ("f32", "f32", "f32"), ("bf16", "f16", "bf16")],
                          ids=lambda d: "-".join(d))
 def test_backward_parity(M, K, N, dts):
@@ -104,3 +108,18 @@ def test_backward_reproducible():
     r2 = _run(X, dY, S, a, b, "bf16", "f16", "f32")
     for u, v in zip(r1[:3], r2[:3]):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("impl", ["wk1", "wk2", "wk4"])
+def test_backward_fused_epilogue_column_groups(impl, monkeypatch):
+    """The gradient epilogue at every column count per wave (16, 32 and 64
+    columns per workgroup), dX in bf16, against the oracle."""
+    monkeypatch.setenv("OBL_DECODE", impl)
+    M, K, N = 16, 1024, 2048
+    X, dY, S, a, b = _case(M, K, N, "bf16", "f16", seed=41)
+    dX, da, db, _ = _run(X, dY, S, a, b, "bf16", "f16", "bf16")
+    rdX, rda, rdb = O.onebit_backward(X, S, a, b, dY)
+    sdx, sda, sdb = O.backward_error_scales(X, a, b, dY)
+    assert O.max_normalised_error(dX, rdX, sdx) <= G.TOL_DECODE + G.BF16_U
+    assert O.max_normalised_error(da, rda, sda) <= G.TOL_DECODE
+    assert O.max_normalised_error(db, rdb, sdb) <= G.TOL_DECODE
