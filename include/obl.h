@@ -23,8 +23,9 @@
  *    is enqueued, and buffers must stay alive until that work completes.
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer
  *    to caller memory after a call returns.  It keeps two scratch buffers per
- *    device: one for the decode kernels' split-K partial sums (M <= 16), the
- *    bf16 copy of the DBF intermediate at prefill sizes, the bf16(x ⊙ b)
+ *    device: one for the split decode kernel's partial sums (M <= 16), the
+ *    bf16 copy of the DBF intermediate at prefill sizes, the exact bf16 terms
+ *    of that intermediate at decode sizes, the bf16(x ⊙ b)
  *    activations the prefill path stages for fp32 or misaligned X, and the
  *    vectors of obl_svid; one for the prefill kernel's split-K partial sums
  *    (grids with few tiles).  Each is allocated with hipMalloc on the first call that
@@ -130,10 +131,13 @@ obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
  *   b [K], m [Kmid], a [N], all scale_dtype (OBL_F32 or OBL_F16).
  *   workspace  float32 [M][Kmid], caller-owned.  When the call's work has
  *              completed it holds T1 = ((X ⊙ b) S2^T) ⊙ m (stage 1, kept in
- *              fp32); stage 2 reads it.  Must not overlap any other argument.
+ *              fp32); stage 2 reads it, or (decode sizes up to 8 rows) the
+ *              exact bf16 terms of T1 that stage 1 also writes into library
+ *              scratch.  Must not overlap any other argument.
  *   Y          [M][N], y_dtype OBL_F32 or OBL_BF16.
  *   Arithmetic: each stage follows obl_linear's rules for the same M
- *   (stage 2 has no input-side scale).
+ *   (stage 2 has no input-side scale; at prefill sizes it reads T1 rounded
+ *   once to bf16).
  *   Errors: as obl_linear.
  */
 obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
