@@ -250,7 +250,7 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   // and the magnitudes) are read before the MFMAs of step s are issued, so
   // their latency hides behind step s; the scheduling barrier keeps the
   // compiler from sinking those reads back to their use.
-  auto compute = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, int t) {
+  auto compute = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, int t, auto&& issue) {
     u32x4 wv[GW_FN];
 #pragma unroll
     for (int c = 0; c < GW_FN; ++c) wv[c] = ws[wcol + 32 * c];
@@ -266,6 +266,7 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
       const int b = s & 1;
       if (s + 1 < GW_S) read_step(s + 1, b ^ 1);
       __builtin_amdgcn_sched_barrier(0);
+      issue(s);   // this step's share of the next stage's DMAs
 #pragma unroll
       for (int c = 0; c < GW_FN; ++c) {
         const uint32_t word = wv[c][s >> 1];
@@ -285,14 +286,22 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   // t + 1.  Prefetch indices are clamped: a redundant reload of the last
   // stage into an idle buffer is harmless.
   auto step = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, u32x4 (*xp)[GW_KT / 8], u32x4* wp, int t) {
-    dma(xp, wp, min(t + 2, nk - 1));
-    compute(xs, ws, t);
+    // The DMAs of stage t + 2 are spread over the k-steps of stage t, one or
+    // two per step between its MFMA groups: issued back to back they stalled
+    // the waves ~650 cycles per stage (the address unit takes ~16 cycles per
+    // 1 KiB transfer) with no MFMA in flight.
+    const uint32_t tn = (uint32_t)(t0 + min(t + 2, nk - 1));
+    compute(xs, ws, t, [&](int s) {
+      if (s < GW_XDMA) dma16(xr, &xp[4 * (GW_XDMA * wave + s)][0], xo[s], tn * (GW_KT * 2));
+      if (s < GW_WDMA) dma16(wr, &wp[64 * (GW_WDMA * wave + s)], wo[s], tn * 16);
+    });
     // vmcnt(10) lgkmcnt(0), then a bare s_barrier: __syncthreads() would also
     // drain the prefetch of stage t + 2 (its fence waits for vmcnt(0)).
     __builtin_amdgcn_s_waitcnt(0x0070 | (GW_XDMA + GW_WDMA));
     __builtin_amdgcn_s_barrier();
   };
   static_assert(GW_XDMA + GW_WDMA < 16, "vmcnt immediate");
+  static_assert(GW_XDMA <= GW_S && GW_WDMA <= GW_S, "every DMA of a stage has a k-step to go with");
   int t = 0;
   for (; t + 3 <= nk; t += 3) {
     step(xa, wa, xc, wc, t);
