@@ -68,7 +68,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GW_THREADS = 256;
-constexpr int GW_BM = 128;        // workgroup rows
 constexpr int GW_WM = 64;         // wave rows
 constexpr int GW_FM = GW_WM / 32; // 2 activation fragments
 constexpr int GW_KT = 128;        // k per stage
@@ -92,20 +91,25 @@ __device__ __forceinline__ u32x4 expand_half(uint32_t h, const u16x2* sh, u32x4 
   return r;
 }
 
-constexpr int GW_XDMA = GW_BM * (GW_KT / 8) / 64 / 4;    // activation DMAs per wave per stage (8)
 constexpr int GW_BTAB_BATCH = 8 * GW_THREADS;             // bf16(b) pairs per table-fill batch
 constexpr double GW_EFF4 = 1.08;                          // per-column cost of the 256-wide tile vs the 448-wide
 
-// Column tiling, by sign fragments (32 columns) per wave: FN = 7 gives the
-// 64 x 224 wave tile and 128 x 448 workgroup tile, FN = 4 a 64 x 128 wave
-// tile and 128 x 256 workgroup tile, FN = 2 a 64 x 64 wave tile and 128 x 128
-// workgroup tile.  Sign columns are staged in whole 256-column DMA rounds
-// (one 16-byte DMA per lane per round; the 128-wide tile uses half of it).
-template <int FN> struct GwTile {
+// Tiling.  Every wave owns 64 rows (two 32-row activation fragments) and FN
+// sign fragments of 32 columns; the four waves stand WR = 2 (rows) x 2
+// (columns) or WR = 1 x 4.  FN = 7, WR = 2: 64 x 224 wave tiles, 128 x 448
+// workgroup tile; FN = 4: 128 x 256; FN = 2: 128 x 128; FN = 1, WR = 1: 64 x
+// 32 wave tiles side by side, a 64 x 128 workgroup tile (for grids that the
+// 128-row tiles leave short of the CUs).  Sign columns are staged in whole
+// 256-column DMA rounds (one 16-byte DMA per lane per round; the 128-wide
+// tiles use half of it).
+template <int FN, int WR = 2> struct GwTile {
   static constexpr int WN = 32 * FN;                      // wave columns
-  static constexpr int BN = 2 * WN;                       // workgroup columns
+  static constexpr int BM = 64 * WR;                      // workgroup rows
+  static constexpr int BN = WN * (4 / WR);                // workgroup columns
   static constexpr int WCOLS = (BN + 255) / 256 * 256;    // sign columns staged
   static constexpr int WDMA = WCOLS / 256;                // sign DMAs per wave per stage
+  static constexpr int XDMA = BM * (GW_KT / 8) / 64 / 4;  // activation DMAs per wave per stage
+  static_assert(WR == 1 || WR == 2, "wave rows");
   static_assert(BN <= 2 * GW_THREADS, "two output scales per thread");
 };
 
@@ -118,14 +122,15 @@ inline int64_t gw_btab_entries(int64_t K) {
 // [s·per, min((s + 1)·per, K/128)) of slice s = b % nsplit, and writes its raw
 // fp32 sums (no output scale) to part[s][M][N]; gemm_split_reduce_kernel adds
 // the slices in order.
-template <typename ST, typename YT, bool PRE, bool SPLIT, int FN>
+template <typename ST, typename YT, bool PRE, bool SPLIT, int FN, int WR>
 __global__ __launch_bounds__(GW_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ W,
                       int64_t N, const ST* __restrict__ pre, const ST* __restrict__ post,
                       YT* __restrict__ Y, bf16_t* __restrict__ Y2, int mt, int nt, int xcd_groups,
                       int nsplit, int per, float* __restrict__ part) {
-  constexpr int GW_WN = GwTile<FN>::WN, GW_BN = GwTile<FN>::BN, GW_FN = FN;
-  constexpr int GW_WCOLS = GwTile<FN>::WCOLS, GW_WDMA = GwTile<FN>::WDMA;
+  using TL = GwTile<FN, WR>;
+  constexpr int GW_WN = TL::WN, GW_BN = TL::BN, GW_FN = FN, GW_BM = TL::BM;
+  constexpr int GW_WCOLS = TL::WCOLS, GW_WDMA = TL::WDMA, GW_XDMA = TL::XDMA;
   // Three stage buffers as distinct LDS objects: the K loop is unrolled by
   // three so every access names its buffer, and the compiler can tell a DMA
   // into one buffer from reads of another.
@@ -141,7 +146,7 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS DMA bases stay scalar
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = WR == 2 ? (wave & 1) : 0, wn = WR == 2 ? (wave >> 1) : wave;
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -479,10 +484,10 @@ int split_count(int64_t tiles, int64_t nk, int num_cus) {
   return (int)std::max<int64_t>(s, 1);
 }
 
-template <typename ST, typename YT, bool PRE, int FN>
+template <typename ST, typename YT, bool PRE, int FN, int WR>
 hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
-  constexpr int BN = GwTile<FN>::BN;
-  const int64_t mt = (a.M + GW_BM - 1) / GW_BM;
+  constexpr int BN = GwTile<FN, WR>::BN, BM = GwTile<FN, WR>::BM;
+  const int64_t mt = (a.M + BM - 1) / BM;
   const int64_t nt = (a.N + BN - 1) / BN;
   const int64_t tiles = mt * nt;
   const int64_t nk = a.K / GW_KT;
@@ -494,7 +499,7 @@ hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
     float* part = nullptr;
     hipError_t e = split_reserve(dev.device, (size_t)nsplit * (size_t)(a.M * a.N), &part);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_wide_kernel<ST, float, PRE, true, FN>), dim3((unsigned)(tiles * nsplit)),
+    hipLaunchKernelGGL((gemm_wide_kernel<ST, float, PRE, true, FN, WR>), dim3((unsigned)(tiles * nsplit)),
                        dim3(GW_THREADS), lds, a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                        static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post), nullptr, nullptr, (int)mt,
                        (int)nt, 1, nsplit, per, part);
@@ -510,37 +515,45 @@ hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
     return hipGetLastError();
   }
   const int xcd = (tiles % 8 == 0) ? 8 : 1;
-  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE, false, FN>), dim3((unsigned)tiles), dim3(GW_THREADS), lds,
+  hipLaunchKernelGGL((gemm_wide_kernel<ST, YT, PRE, false, FN, WR>), dim3((unsigned)tiles), dim3(GW_THREADS), lds,
                      a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                      static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post),
                      static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.Y2), (int)mt, (int)nt, xcd, 1, 0, nullptr);
   return hipGetLastError();
 }
 
-// Column-tile width.  A grid that would split K with the 256-wide tile takes
-// the 128-wide one (twice the tiles, half the slices: half the partial-sum
-// traffic).  Same-box timings, 128 vs 256 vs 448 wide, us: 512x3072x4096
-// 30.2 / 33.2 / 37.2, 512x4096x4096 32.8 / 35.9 / 41.6, 1024x4096x4096
-// 39.7 / 47.2 / 55.9, 256x4096x4096 26.1 / 32.5 / 36.7, 512x4096x3072
-// 31.1 / 30.4 / 38.3, the DBF prefill 512x4096->3072->4096 61.2 / 64.7 /
-// 78.3.  Otherwise the estimated time is the number of rounds of one
+// Tile.  A grid that would split K with the 128 x 256 tile takes the 64 x 128
+// tile when that grid fits one workgroup per CU (no split at all at M = 512,
+// N = 3072 or 4096), else the 128 x 128 tile (twice the tiles of the 256-wide
+// one, half the slices: half the partial-sum traffic).  Same-box timings,
+// 64 x 128 / 128 x 128 / 128 x 256, us: 512x4096x3072 21.7 / 29.6 / 31.2,
+// 512x3072x4096 19.9 / 30.3 / 33.6, 512x4096x4096 24.3 / 33.0 / 36.4,
+// 256x4096x4096 21.7 / 26.0 / 32.2, 128x4096x4096 16.4 / 21.8 / 25.0,
+// 64x4096x14336 21.3 / 26.5 / 28.8, the DBF prefill 512x4096->3072->4096
+// 43.3 / 59.3 / 65.3; 1024x4096x4096 (512 of the small tiles: two rounds)
+// 45.1 / 39.3 / 48.0.  Otherwise the estimated time is the number of rounds of one
 // workgroup per CU times the tile width, with `GW_EFF4` the relative
 // per-column cost of the 256-wide tile against the 448-wide one.  Measured at
 // M = 2048, K = 4096: N = 14336 keeps 448 (217 vs 245 us), N = 11008 and
 // N = 4096 take 256 (182 vs 198 us, 67 vs 96 us; the 128-wide tile 77 us).
-// OBL_GEMM=w2 / w4 / w7 forces a width (tests).
+// OBL_GEMM=w1 / w2 / w4 / w7 forces a tile (tests).
 int64_t rounds(int64_t M, int64_t N, int bn, int cus) {
-  const int64_t tiles = ((M + GW_BM - 1) / GW_BM) * ((N + bn - 1) / bn);
+  const int64_t tiles = ((M + 127) / 128) * ((N + bn - 1) / bn);
   return (tiles + cus - 1) / cus;
 }
 
+// Returns FN for the 128-row tiles, or 1 for the 64 x 128 tile (WR = 1).
 int pick_fn(int64_t M, int64_t N, int cus) {
   const char* e = std::getenv("OBL_GEMM");
+  if (e && e[0] == 'w' && e[1] == '1') return 1;
   if (e && e[0] == 'w' && e[1] == '2') return 2;
   if (e && e[0] == 'w' && e[1] == '4') return 4;
   if (e && e[0] == 'w' && e[1] == '7') return 7;
-  const int64_t tiles4 = ((M + GW_BM - 1) / GW_BM) * ((N + GwTile<4>::BN - 1) / GwTile<4>::BN);
-  if (tiles4 * 2 <= cus) return 2;
+  const int64_t tiles4 = ((M + 127) / 128) * ((N + GwTile<4>::BN - 1) / GwTile<4>::BN);
+  if (tiles4 * 2 <= cus) {
+    const int64_t tiles1 = ((M + 63) / 64) * ((N + GwTile<1, 1>::BN - 1) / GwTile<1, 1>::BN);
+    return tiles1 <= cus ? 1 : 2;
+  }
   const double u4 = (double)rounds(M, N, GwTile<4>::BN, cus) * GwTile<4>::BN * GW_EFF4;
   const double u7 = (double)rounds(M, N, GwTile<7>::BN, cus) * GwTile<7>::BN;
   return u4 < u7 ? 4 : 7;
@@ -549,8 +562,9 @@ int pick_fn(int64_t M, int64_t N, int cus) {
 template <typename ST, typename YT, bool PRE>
 hipError_t launch(const LinearArgs& a, const DeviceInfo& dev) {
   const int fn = pick_fn(a.M, a.N, dev.num_cus);
-  if (fn == 2) return launch_fn<ST, YT, PRE, 2>(a, dev);
-  return fn == 4 ? launch_fn<ST, YT, PRE, 4>(a, dev) : launch_fn<ST, YT, PRE, 7>(a, dev);
+  if (fn == 1) return launch_fn<ST, YT, PRE, 1, 1>(a, dev);
+  if (fn == 2) return launch_fn<ST, YT, PRE, 2, 2>(a, dev);
+  return fn == 4 ? launch_fn<ST, YT, PRE, 4, 2>(a, dev) : launch_fn<ST, YT, PRE, 7, 2>(a, dev);
 }
 
 template <typename ST>
@@ -664,7 +678,7 @@ bool gemm_wide_shape_ok(int64_t M, int64_t K, int64_t N, bool has_pre, const voi
   // out-of-range sentinel), and the grid in an int.
   const int64_t lim = (int64_t)0xFFFFF000u;
   if (a.M * a.K * 2 > lim || a.N * (a.K / 32) * 4 > lim) return false;
-  const int64_t tiles = ((a.M + GW_BM - 1) / GW_BM) * ((a.N + GwTile<2>::BN - 1) / GwTile<2>::BN);
+  const int64_t tiles = ((a.M + 63) / 64) * ((a.N + GwTile<1, 1>::BN - 1) / GwTile<1, 1>::BN);
   if (tiles > 0x7fffffff) return false;
   // LDS: the bf16(b) table (2K bytes rounded up to 8 KiB batches, dynamic)
   // next to ~124 KiB of static stage buffers.

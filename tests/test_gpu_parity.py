@@ -100,12 +100,12 @@ GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("bf16", "f32", 
 
 @pytest.mark.parametrize("M,K,N", GEMM_CASES)
 @pytest.mark.parametrize("dts", GEMM_DTYPES, ids=lambda d: "-".join(d))
-@pytest.mark.parametrize("impl", ["auto", "w7", "w4", "w2", "v2", "v1"])
+@pytest.mark.parametrize("impl", ["auto", "w7", "w4", "w2", "w1", "v2", "v1"])
 def test_gemm_path(M, K, N, dts, impl, monkeypatch):
     """impl=auto picks the main 32x32 kernel where it applies (K % 128 == 0;
-    fp32 or misaligned x through the prescale pass) and its tile width; w7 / w4 /
-    w2 force the 448- / 256- / 128-column tile, v2 the LDS-staged 16x16
-    kernel, v1 the 8-wave kernel."""
+    fp32 or misaligned x through the prescale pass) and its tile; w7 / w4 / w2
+    force the 128-row tiles of 448 / 256 / 128 columns, w1 the 64 x 128 tile,
+    v2 the LDS-staged 16x16 kernel, v1 the 8-wave kernel."""
     if impl != "auto":
         monkeypatch.setenv("OBL_GEMM", impl)
     G.say(f"gemm[{impl}] M={M} K={K} N={N} {dts}")
