@@ -39,6 +39,14 @@
 //  * Three stage buffers, one barrier per stage: stages t + 1 and t + 2 are
 //    in flight while stage t is computed (two stages of latency cover the
 //    misses of the streamed sign words, one line per column per 8 stages).
+//  * The sign operands of k-step s + 1 are expanded between the MFMAs of
+//    step s, into registers of their own, and the barrier sits inside the
+//    last k-step of a stage, so the next stage's step-0 operands are
+//    expanded under that step's MFMAs.  With one operand register set reused
+//    for all columns (the compiler's choice) expansion and MFMAs ran one
+//    after the other: 2048 x 4096 x 14336 took 210 us, 192-197 us now.  The
+//    expansion is still ~13 % of the kernel's time (measured by removing
+//    it); the clock then runs at ~1.5 GHz, power-limited.
 //  * Out-of-range rows / columns re-read the last valid one and are not
 //    stored; every load is unconditional.
 //  * Epilogue: acc·a in fp32 (a staged in LDS), one cast to the output dtype.
@@ -251,70 +259,105 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
 #pragma unroll
     for (int i = 0; i < GW_FM; ++i) acc[c][i] = f32x16{};
 
-  // One stage.  The LDS operands of k-step s + 1 (two activation fragments
-  // and the magnitudes) are read before the MFMAs of step s are issued, so
-  // their latency hides behind step s; the scheduling barrier keeps the
-  // compiler from sinking those reads back to their use.
-  auto compute = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, int t, auto&& issue) {
-    u32x4 wv[GW_FN];
+  // Operand registers.  wv: the current stage's packed sign words (128 k per
+  // column); mg: its bf16(b) pairs, one quad per k-step; xf: activation
+  // fragments of two k-steps; av: sign operands of two k-steps.  Operands of
+  // step s + 1 are formed while the MFMAs of step s run, into registers of
+  // their own: the expansion of a k-step then costs no matrix-core time.
+  u32x4 wv[GW_FN], mg[GW_S], xf[2][GW_FM], av[2][GW_FN];
+  auto half = [&](int c, int s) -> uint32_t {
+    const uint32_t word = wv[c][s >> 1];
+    return (s & 1) ? (word >> 16) : (word & 0xFFFFu);
+  };
+  // First reads of stage t: sign words, magnitudes, step-0 activations.  The
+  // magnitude index is clamped: the last stage also reads a (redundant) next
+  // stage, see below.
+  auto load_stage = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, int t) {
+    const int tm = min(t, nk - 1);
 #pragma unroll
     for (int c = 0; c < GW_FN; ++c) wv[c] = ws[wcol + 32 * c];
-    u32x4 xf[2][GW_FM], mg[2];
-    auto read_step = [&](int s, int b) {
-      mg[b] = PRE ? bt4[((t0 + t) * GW_KT + 16 * s + 8 * g) >> 3] : ones;
 #pragma unroll
-      for (int i = 0; i < GW_FM; ++i) xf[b][i] = xs[xrow + 32 * i][(2 * s + g) ^ (lane & 15)];
-    };
-    read_step(0, 0);
+    for (int s = 0; s < GW_S; ++s) mg[s] = PRE ? bt4[((t0 + tm) * GW_KT + 16 * s + 8 * g) >> 3] : ones;
 #pragma unroll
-    for (int s = 0; s < GW_S; ++s) {
-      const int b = s & 1;
-      if (s + 1 < GW_S) read_step(s + 1, b ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(s);   // this step's share of the next stage's DMAs
+    for (int i = 0; i < GW_FM; ++i) xf[0][i] = xs[xrow + 32 * i][g ^ (lane & 15)];
+  };
+  // The MFMAs of column fragment c at k-step s (operand set b), with the
+  // expansion of another operand (column cn, step sn, into set bn) between
+  // the first and the second.
+  auto group = [&](int b, int c, bool expand, int bn, int cn, int sn) {
+    acc[c][0] = mfma32(av[b][c], xf[b][0], acc[c][0]);
+    if (expand) av[bn][cn] = expand_half(half(cn, sn), sh, mg[sn]);
 #pragma unroll
-      for (int c = 0; c < GW_FN; ++c) {
-        const uint32_t word = wv[c][s >> 1];
-        const u32x4 a = expand_half((s & 1) ? (word >> 16) : (word & 0xFFFFu), sh, mg[b]);
+    for (int i = 1; i < GW_FM; ++i) acc[c][i] = mfma32(av[b][c], xf[b][i], acc[c][i]);
+  };
+  auto interleave = [&](int groups) {   // MFMA, 4 VALU, MFMA, 4 VALU per group
 #pragma unroll
-        for (int i = 0; i < GW_FM; ++i) acc[c][i] = mfma32(a, xf[b][i], acc[c][i]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int c = 0; c < groups; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, GW_FM - 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
   };
 
-  // One barrier per stage, prefetch distance two.  Step t issues the DMA of
-  // stage t + 2 into the buffer that stage t - 1 used (every wave finished
-  // reading it before the previous barrier), computes stage t, then waits
-  // for its own DMA of stage t + 1 (all but the GW_XDMA + GW_WDMA most recent
-  // transfers) and meets the others at the barrier, which publishes stage
-  // t + 1.  Prefetch indices are clamped: a redundant reload of the last
-  // stage into an idle buffer is harmless.
-  auto step = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, u32x4 (*xp)[GW_KT / 8], u32x4* wp, int t) {
-    // The DMAs of stage t + 2 are spread over the k-steps of stage t, one or
-    // two per step between its MFMA groups: issued back to back they stalled
-    // the waves ~650 cycles per stage (the address unit takes ~16 cycles per
-    // 1 KiB transfer) with no MFMA in flight.
+  // One stage: k-steps 0..6 read the activations of the next step, issue
+  // their share of the DMAs of stage t + 2 (into the buffer stage t - 1
+  // used) and run their MFMAs with the next step's sign operands expanded in
+  // between.  Issued back to back the DMAs stalled the waves ~650 cycles per
+  // stage (the address unit takes ~16 cycles per 1 KiB transfer) with no MFMA
+  // in flight.  Step 7 waits for this wave's DMAs of stage t + 1 (all but the
+  // GW_XDMA + GW_WDMA most recent transfers) and for its LDS reads, issues
+  // the first column's MFMAs, meets the other waves at the barrier (which
+  // publishes stage t + 1 and retires stage t's buffer), then reads stage
+  // t + 1's first operands and expands its step-0 signs under the remaining
+  // MFMAs.  Prefetch indices are clamped: a redundant reload of the last
+  // stage into an idle buffer is harmless, and so is reading it.
+  auto step = [&](u32x4 (*xs)[GW_KT / 8], u32x4 (*xn)[GW_KT / 8], const u32x4* wn_, u32x4 (*xp)[GW_KT / 8],
+                  u32x4* wp, int t) {
     const uint32_t tn = (uint32_t)(t0 + min(t + 2, nk - 1));
-    compute(xs, ws, t, [&](int s) {
-      if (s < GW_XDMA) dma16(xr, &xp[4 * (GW_XDMA * wave + s)][0], xo[s], tn * (GW_KT * 2));
+#pragma unroll
+    for (int s = 0; s + 1 < GW_S; ++s) {
+      const int b = s & 1;
+#pragma unroll
+      for (int i = 0; i < GW_FM; ++i) xf[b ^ 1][i] = xs[xrow + 32 * i][(2 * (s + 1) + g) ^ (lane & 15)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = s; i < GW_XDMA; i += GW_S - 1)
+        dma16(xr, &xp[4 * (GW_XDMA * wave + i)][0], xo[i], tn * (GW_KT * 2));
       if (s < GW_WDMA) dma16(wr, &wp[64 * (GW_WDMA * wave + s)], wo[s], tn * 16);
-    });
-    // vmcnt(10) lgkmcnt(0), then a bare s_barrier: __syncthreads() would also
-    // drain the prefetch of stage t + 2 (its fence waits for vmcnt(0)).
-    __builtin_amdgcn_s_waitcnt(0x0070 | (GW_XDMA + GW_WDMA));
+#pragma unroll
+      for (int c = 0; c < GW_FN; ++c) group(b, c, true, b ^ 1, c, s + 1);
+      interleave(GW_FN);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int bl = (GW_S - 1) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0070 | (GW_XDMA + GW_WDMA));   // vmcnt(n) lgkmcnt(0)
+    group(bl, 0, false, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(xn, wn_, t + 1);
+#pragma unroll
+    for (int c = 1; c < GW_FN; ++c) group(bl, c, true, 0, c - 1, 0);
+    interleave(GW_FN - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    av[0][GW_FN - 1] = expand_half(half(GW_FN - 1, 0), sh, mg[0]);
+    __builtin_amdgcn_sched_barrier(0);
   };
   static_assert(GW_XDMA + GW_WDMA < 16, "vmcnt immediate");
-  static_assert(GW_XDMA <= GW_S && GW_WDMA <= GW_S, "every DMA of a stage has a k-step to go with");
+  static_assert(GW_WDMA <= GW_S - 1, "every sign DMA of a stage has a k-step to go with");
+
+  load_stage(xa, wa, 0);
+#pragma unroll
+  for (int c = 0; c < GW_FN; ++c) av[0][c] = expand_half(half(c, 0), sh, mg[0]);
   int t = 0;
   for (; t + 3 <= nk; t += 3) {
-    step(xa, wa, xc, wc, t);
-    step(xb, wb, xa, wa, t + 1);
-    step(xc, wc, xb, wb, t + 2);
+    step(xa, xb, wb, xc, wc, t);
+    step(xb, xc, wc, xa, wa, t + 1);
+    step(xc, xa, wa, xb, wb, t + 2);
   }
-  if (t < nk) step(xa, wa, xc, wc, t);
-  if (t + 1 < nk) step(xb, wb, xa, wa, t + 1);
+  if (t < nk) step(xa, xb, wb, xc, wc, t);
+  if (t + 1 < nk) step(xb, xc, wc, xa, wa, t + 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);     // no DMA may still target LDS when the block ends
 
   // Epilogue.  acc[c][i][4q + e] = D[row n = 8q + 4g + e][col m = l32] of the
