@@ -260,37 +260,35 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
     for (int i = 0; i < GW_FM; ++i) acc[c][i] = f32x16{};
 
   // Operand registers.  wv: the current stage's packed sign words (128 k per
-  // column); mg: its bf16(b) pairs, one quad per k-step; xf: activation
-  // fragments of two k-steps; av: sign operands of two k-steps.  Operands of
-  // step s + 1 are formed while the MFMAs of step s run, into registers of
-  // their own: the expansion of a k-step then costs no matrix-core time.
-  u32x4 wv[GW_FN], mg[GW_S], xf[2][GW_FM], av[2][GW_FN];
+  // column); mr: bf16(b) pair quads of two k-steps (by step parity); xf:
+  // activation fragments of two k-steps; av: sign operands of two k-steps.
+  // Operands of step s + 1 are formed while the MFMAs of step s run, into
+  // registers of their own: the expansion of a k-step then costs no
+  // matrix-core time.
+  u32x4 wv[GW_FN], mr[2], xf[2][GW_FM], av[2][GW_FN];
   auto half = [&](int c, int s) -> uint32_t {
     const uint32_t word = wv[c][s >> 1];
     return (s & 1) ? (word >> 16) : (word & 0xFFFFu);
   };
-  // First reads of stage t: sign words, magnitudes, step-0 activations.  The
-  // magnitude index is clamped: the last stage also reads a (redundant) next
-  // stage, see below.
-  auto load_stage = [&](u32x4 (*xs)[GW_KT / 8], const u32x4* ws, int t) {
-    const int tm = min(t, nk - 1);
-#pragma unroll
-    for (int c = 0; c < GW_FN; ++c) wv[c] = ws[wcol + 32 * c];
-#pragma unroll
-    for (int s = 0; s < GW_S; ++s) mg[s] = PRE ? bt4[((t0 + tm) * GW_KT + 16 * s + 8 * g) >> 3] : ones;
-#pragma unroll
-    for (int i = 0; i < GW_FM; ++i) xf[0][i] = xs[xrow + 32 * i][g ^ (lane & 15)];
+  // Magnitudes of k-step s (possibly past the stage's last) of stage t.  The
+  // table is static, so they are read two k-steps ahead of their use; the
+  // stage is clamped to the block's last.
+  auto mag = [&](int t, int s) -> u32x4 {
+    if constexpr (!PRE) return ones;
+    const int ts = min(t + s / GW_S, nk - 1);
+    return bt4[((t0 + ts) * GW_KT + 16 * (s % GW_S) + 8 * g) >> 3];
   };
   // The MFMAs of column fragment c at k-step s (operand set b), with the
-  // expansion of another operand (column cn, step sn, into set bn) between
-  // the first and the second.
+  // expansion of another operand (column cn of step sn, into set bn, with the
+  // magnitudes mr[sn & 1]) between the first and the second.
   auto group = [&](int b, int c, bool expand, int bn, int cn, int sn) {
     acc[c][0] = mfma32(av[b][c], xf[b][0], acc[c][0]);
-    if (expand) av[bn][cn] = expand_half(half(cn, sn), sh, mg[sn]);
+    if (expand) av[bn][cn] = expand_half(half(cn, sn), sh, mr[sn & 1]);
 #pragma unroll
     for (int i = 1; i < GW_FM; ++i) acc[c][i] = mfma32(av[b][c], xf[b][i], acc[c][i]);
   };
-  auto interleave = [&](int groups) {   // MFMA, 4 VALU, MFMA, 4 VALU per group
+  // Issue order of a k-step: MFMA, 4 VALU, MFMA, 4 VALU per column fragment.
+  auto interleave = [&](int groups) {
 #pragma unroll
     for (int c = 0; c < groups; ++c) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -300,18 +298,17 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
     }
   };
 
-  // One stage: k-steps 0..6 read the activations of the next step, issue
-  // their share of the DMAs of stage t + 2 (into the buffer stage t - 1
-  // used) and run their MFMAs with the next step's sign operands expanded in
-  // between.  Issued back to back the DMAs stalled the waves ~650 cycles per
-  // stage (the address unit takes ~16 cycles per 1 KiB transfer) with no MFMA
-  // in flight.  Step 7 waits for this wave's DMAs of stage t + 1 (all but the
-  // GW_XDMA + GW_WDMA most recent transfers) and for its LDS reads, issues
-  // the first column's MFMAs, meets the other waves at the barrier (which
-  // publishes stage t + 1 and retires stage t's buffer), then reads stage
-  // t + 1's first operands and expands its step-0 signs under the remaining
-  // MFMAs.  Prefetch indices are clamped: a redundant reload of the last
-  // stage into an idle buffer is harmless, and so is reading it.
+  // One stage: k-steps 0..6 read the activations of the next step and the
+  // magnitudes of the step after, issue their share of the DMAs of stage
+  // t + 2 (into the buffer stage t - 1 used) and run their MFMAs with the
+  // next step's sign operands expanded in between.  Step 7 waits for this
+  // wave's DMAs of stage t + 1 (all but the GW_XDMA + GW_WDMA most recent
+  // transfers) and for its LDS reads, issues the first column's MFMAs, meets
+  // the other waves at the barrier (which publishes stage t + 1 and retires
+  // stage t's buffer), then reads stage t + 1's sign words and first
+  // activations and expands its step-0 signs under the remaining MFMAs.
+  // Prefetch indices are clamped: a redundant reload of the last stage into
+  // an idle buffer is harmless, and so is reading it.
   auto step = [&](u32x4 (*xs)[GW_KT / 8], u32x4 (*xn)[GW_KT / 8], const u32x4* wn_, u32x4 (*xp)[GW_KT / 8],
                   u32x4* wp, int t) {
     const uint32_t tn = (uint32_t)(t0 + min(t + 2, nk - 1));
@@ -320,14 +317,26 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
       const int b = s & 1;
 #pragma unroll
       for (int i = 0; i < GW_FM; ++i) xf[b ^ 1][i] = xs[xrow + 32 * i][(2 * (s + 1) + g) ^ (lane & 15)];
+      mr[b] = mag(t, s + 2);
       __builtin_amdgcn_sched_barrier(0);
+      // This step's DMAs: activation transfers s, s + 7, ..., then sign
+      // transfer s.  Transfer d goes with column group d % GW_FN, in a
+      // scheduling region of its own, so the ~40 cycles a DMA holds the wave
+      // overlap that group's MFMAs rather than stacking up in front of one.
+      const int nx = s < GW_XDMA ? (GW_XDMA - 1 - s) / (GW_S - 1) + 1 : 0;
+      const int nd = nx + (s < GW_WDMA ? 1 : 0);
 #pragma unroll
-      for (int i = s; i < GW_XDMA; i += GW_S - 1)
-        dma16(xr, &xp[4 * (GW_XDMA * wave + i)][0], xo[i], tn * (GW_KT * 2));
-      if (s < GW_WDMA) dma16(wr, &wp[64 * (GW_WDMA * wave + s)], wo[s], tn * 16);
+      for (int c = 0; c < GW_FN; ++c) {
+        group(b, c, true, b ^ 1, c, s + 1);
 #pragma unroll
-      for (int c = 0; c < GW_FN; ++c) group(b, c, true, b ^ 1, c, s + 1);
-      interleave(GW_FN);
+        for (int d = c; d < nd; d += GW_FN) {
+          if (d < nx) dma16(xr, &xp[4 * (GW_XDMA * wave + s + (GW_S - 1) * d)][0], xo[s + (GW_S - 1) * d],
+                            tn * (GW_KT * 2));
+          else dma16(wr, &wp[64 * (GW_WDMA * wave + s)], wo[s], tn * 16);
+        }
+        interleave(1);
+        if (c < nd) __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     constexpr int bl = (GW_S - 1) & 1;
@@ -336,20 +345,30 @@ void gemm_wide_kernel(const bf16_t* __restrict__ X, int64_t M, int64_t K, const 
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    load_stage(xn, wn_, t + 1);
+#pragma unroll
+    for (int c = 0; c < GW_FN; ++c) wv[c] = wn_[wcol + 32 * c];
+#pragma unroll
+    for (int i = 0; i < GW_FM; ++i) xf[0][i] = xn[xrow + 32 * i][g ^ (lane & 15)];
+    mr[1] = mag(t, GW_S + 1);
 #pragma unroll
     for (int c = 1; c < GW_FN; ++c) group(bl, c, true, 0, c - 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, GW_FN + GW_FM + 1, 0);
     interleave(GW_FN - 1);
     __builtin_amdgcn_sched_barrier(0);
-    av[0][GW_FN - 1] = expand_half(half(GW_FN - 1, 0), sh, mg[0]);
+    av[0][GW_FN - 1] = expand_half(half(GW_FN - 1, 0), sh, mr[0]);
     __builtin_amdgcn_sched_barrier(0);
   };
   static_assert(GW_XDMA + GW_WDMA < 16, "vmcnt immediate");
   static_assert(GW_WDMA <= GW_S - 1, "every sign DMA of a stage has a k-step to go with");
 
-  load_stage(xa, wa, 0);
 #pragma unroll
-  for (int c = 0; c < GW_FN; ++c) av[0][c] = expand_half(half(c, 0), sh, mg[0]);
+  for (int c = 0; c < GW_FN; ++c) wv[c] = wa[wcol + 32 * c];
+#pragma unroll
+  for (int i = 0; i < GW_FM; ++i) xf[0][i] = xa[xrow + 32 * i][g ^ (lane & 15)];
+  mr[0] = mag(0, 0);
+  mr[1] = mag(0, 1);
+#pragma unroll
+  for (int c = 0; c < GW_FN; ++c) av[0][c] = expand_half(half(c, 0), sh, mr[0]);
   int t = 0;
   for (; t + 3 <= nk; t += 3) {
     step(xa, xb, wb, xc, wc, t);
