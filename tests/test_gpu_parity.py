@@ -88,11 +88,13 @@ def test_decode_path(M, K, N, dts):
 # Small grids split K (bf16 x, K % 128 == 0): (256, 4096, 224) and (600, 4096, 449)
 # into 8 slices, (300, 1152, 672) into 2, (40, 2048, 98) into 4 with N % 4 != 0
 # (scalar partials and reduction), (200, 4736, 1000) into 8 uneven slices (37
-# stages of 128 k); (255, 512, 448) has too few stages to split.
+# stages of 128 k); (255, 512, 448) has too few stages to split.  K = 128,
+# 256 and 640 run 1, 2 and 5 stages whole (the stage loop is unrolled by three;
+# the last stage also reads a clamped next stage).
 GEMM_CASES = [
     (17, 32, 16), (64, 96, 225), (255, 512, 448), (256, 4096, 224), (257, 160, 1000),
     (600, 4096, 449), (33, 64, 33), (513, 384, 230), (300, 1152, 672), (40, 2048, 98),
-    (200, 4736, 1000),
+    (200, 4736, 1000), (130, 128, 500), (70, 256, 257), (129, 640, 449),
 ]
 GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("bf16", "f32", "bf16"),
                ("f32", "f32", "f32"), ("f32", "f16", "bf16")]
@@ -234,6 +236,21 @@ def test_integer_exact_bitwise(path, M, K, N):
     G.say(f"int-exact {path} M={M} K={K} N={N}")
     c = WL.onebit_case(M, K, N, "bf16", "f16", "f32", kind="int_exact", seed=K + N)
     Y = G.run_onebit(c, path)
+    assert np.array_equal(Y, O.onebit_linear(c.X, c.W_sign, c.a, c.b))
+
+
+@pytest.mark.parametrize("impl", ["w7", "w4", "w2", "w1"])
+@pytest.mark.parametrize("M,K,N", [(300, 4096, 500), (129, 640, 449), (130, 128, 500), (70, 256, 257),
+                                   (513, 384, 230)])
+def test_integer_exact_gemm_tiles(M, K, N, impl, monkeypatch):
+    """Every tile of the main prefill kernel, whole K over 1, 2, 3, 5 and 32
+    stages (and split K where the grid is small): integer-valued inputs make
+    every partial sum exact in fp32, so the result equals the oracle bit for
+    bit whatever the order of accumulation."""
+    monkeypatch.setenv("OBL_GEMM", impl)
+    G.say(f"int-exact gemm[{impl}] M={M} K={K} N={N}")
+    c = WL.onebit_case(M, K, N, "bf16", "f16", "f32", kind="int_exact", seed=K + N + M)
+    Y = G.run_onebit(c, "gemm")
     assert np.array_equal(Y, O.onebit_linear(c.X, c.W_sign, c.a, c.b))
 
 
