@@ -52,16 +52,17 @@
 //  * Epilogue: acc·a in fp32 (a staged in LDS), one cast to the output dtype.
 //    A lane holds four consecutive output columns per register quad, written
 //    as one 16-byte (fp32) or 8-byte (bf16) store.
-//  * Small grids (at most half as many tiles as CUs, e.g. M = 512 with
-//    N = 3072 is 28 tiles) split K: tiles x slices fill the CUs once, each
-//    slice writes fp32 partial sums and a second kernel adds the slices in
-//    order (fixed order: reproducible; accumulation stays fp32).  Measured
-//    on 512 x 4096 x 3072: 8 slices of 4 stages, 224 workgroups, ~31 us for
-//    the split kernel and ~11 us for the reduction, against ~99 us unsplit
-//    on 28 workgroups.  The split kernel's fixed cost is the burst of
-//    partial sums written when every workgroup ends together (51 MB here)
-//    and the reduction reading them back; counting that traffic, more
-//    slices of fewer stages stop paying at about 8.
+//  * Small grids first take smaller tiles (64 x 128 when that grid fits the
+//    CUs once: M = 512, N = 3072 is 192 tiles, whole K each), and a grid
+//    still at most half as many tiles as CUs splits K: tiles x slices fill
+//    the CUs once, each slice writes fp32 partial sums and a second kernel
+//    adds the slices in order (fixed order: reproducible; accumulation stays
+//    fp32).  Measured on 512 x 4096 x 3072 with the 448-wide tile (28 tiles):
+//    8 slices of 4 stages, ~31 us for the split kernel and ~11 us for the
+//    reduction, against ~99 us unsplit.  The split kernel's fixed cost is the
+//    burst of partial sums written when every workgroup ends together and
+//    the reduction reading them back; more slices of fewer stages stop
+//    paying at about 8.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
