@@ -339,6 +339,18 @@ def main():
         f"(GEMV {ms_launch * 1e3:.2f} us)")
     del srcs, dst, tc
     torch.cuda.empty_cache()
+    # The fixed cost of a launch in the same arrangement: a kernel that spins for zero cycles
+    # (torch's own test helper), R of them in one graph replay.  No kernel launched this way
+    # takes less; what the GEMV and the copy add on top of it is their memory and arithmetic.
+    try:
+        te = Timed(torch, [(lambda: torch.cuda._sleep(0)) for _ in range(R)])
+        _, ms_empty = te.run(args.warmup, args.steps)
+        out["launch_floor_context"]["empty_kernel_us_per_launch"] = round(ms_empty * 1e3, 4)
+        out["launch_floor_context"]["gemv_above_empty_us"] = round((ms_launch - ms_empty) * 1e3, 4)
+        log(f"[bench] context: empty kernel {ms_empty * 1e3:.2f} us per launch")
+        del te
+    except (AttributeError, RuntimeError) as e:   # helper missing on this build
+        log(f"[bench] context: no empty-kernel timing ({e})")
 
     # ---------------- secondary workloads
     if not args.no_secondary:
