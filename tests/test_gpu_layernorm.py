@@ -64,10 +64,11 @@ def _affine(rng, N, kind, dt):
 
 
 # Every kernel variant: 1024-thread register path with 4 and 8 chunks (M < 256),
-# 256-thread with 4, 8 and 16 chunks, the vector window path (rows too long
+# 256-thread with 4 and 8 chunks, 512-thread with 8 (rows of 2 K..4 K vectors,
+# (300, 14336) and (270, 9000)), the vector window path (rows too long
 # for registers) and the scalar window path (N % 4 != 0), plus tiny rows.
 SHAPES = [(1, 11008), (4, 4096), (3, 1000), (16, 14336), (3, 20000), (256, 4096), (260, 8000),
-          (300, 14336), (257, 4097), (2, 70000), (300, 70001), (5, 1), (2, 3), (1, 64)]
+          (300, 14336), (270, 9000), (257, 4097), (2, 70000), (300, 70001), (5, 1), (2, 3), (1, 64)]
 
 
 @pytest.mark.parametrize("M,N", SHAPES)
