@@ -436,7 +436,7 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         ms8 = ev0.elapsed_time(ev1) / 3
-        passes = 2 * 32 + 2                      # |W| reads: two per iteration, the final row pass, Sign(W)
+        passes = 32 + 2                          # |W| reads: one per (fused) iteration, the final row pass, Sign(W)
         sec["svid-11008x4096-f16-32iters"] = {"ms_per_conversion": round(ms8, 3),
                                               "weight_read_GBps": round(passes * Wd.numel() * 2 / (ms8 * 1e-3) / 1e9, 1)}
         log(f"[bench] svid-11008x4096-f16-32iters: {ms8:.3f} ms per conversion")

@@ -260,6 +260,127 @@ __global__ __launch_bounds__(256) void svid_cols_kernel(const WT* __restrict__ W
   for (int e = 0; e < CV; ++e) part[c * K + k + e] = acc[e];
 }
 
+// ---------------------------------------------------------------- fused pass
+// One read of W per iteration (rows of at most 512·V elements): a workgroup
+// of 4 waves takes rows [rb, rb + rpw), two per wave at a time (the next two
+// already loading), with v in LDS.  From the same registers it forms
+// u_i = |W_i| · v / ||v|| and adds |W_ik| u_i into per-lane column sums, so
+// the column pass no longer reads W again.  At the end the four waves' column
+// sums are added in wave order into part[block][K], and upart[block] = Σ u_i^2
+// over its rows (rows in order within a wave, then the waves in order).  The
+// column reduction then forms v from the blocks' partial rows as before.
+// Element (j, e) of lane l is column (64 j + l) · V + e (j < SV_FJ).
+constexpr int SV_FJ = 8;
+template <typename WT, int V>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void svid_fused_kernel(const WT* __restrict__ W, int64_t N, int64_t K, int64_t rpw, const float* __restrict__ v,
+                       float* __restrict__ u, float* __restrict__ upart, float* __restrict__ part,
+                       float* __restrict__ sink) {
+  using RT = typename Raw<V, WT>::type;
+  constexpr int KMAX = 64 * SV_FJ * V;
+  __shared__ __align__(16) float vs[KMAX];
+  __shared__ __align__(16) float cs[4][KMAX];
+  __shared__ float red[4];
+  __shared__ float usw[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // v into LDS and ||v||^2 (the same fixed order in every workgroup).
+  float vsq = 0.f;
+#pragma unroll
+  for (int i = 0; i < KMAX / 1024; ++i) {
+    const int f = (256 * i + tid) * 4;
+    const bool okv = f < K;
+    const float4 t = *reinterpret_cast<const float4*>(v + (okv ? f : 0));
+    reinterpret_cast<float4*>(vs)[f >> 2] = t;
+    vsq += okv ? ((t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w)) : 0.f;
+  }
+  const float vnorm = sqrtf(block_sum(vsq, red));   // its barrier also publishes vs
+
+  const int64_t rb = (int64_t)blockIdx.x * rpw, re = min(rb + rpw, N);
+  int ec[SV_FJ];
+  bool ok[SV_FJ];
+#pragma unroll
+  for (int j = 0; j < SV_FJ; ++j) {
+    const int e = (64 * j + lane) * V;
+    ok[j] = e < K;
+    ec[j] = ok[j] ? e : (int)K - V;
+  }
+  auto load = [&](int64_t r, RT (&q)[SV_FJ]) {   // rows past N re-read row N - 1 (unused)
+    const WT* w = W + min(r, N - 1) * K;
+#pragma unroll
+    for (int j = 0; j < SV_FJ; ++j) q[j] = Raw<V, WT>::load(w + ec[j]);
+  };
+  float cp[SV_FJ][V];
+#pragma unroll
+  for (int j = 0; j < SV_FJ; ++j)
+#pragma unroll
+    for (int e = 0; e < V; ++e) cp[j][e] = 0.f;
+  float usq = 0.f;
+  // Rows r and r + 1 from q0, q1: dot products, u, column sums.
+  auto process = [&](int64_t r, const RT (&q0)[SV_FJ], const RT (&q1)[SV_FJ]) {
+    float a0[SV_FJ][V], a1[SV_FJ][V];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < SV_FJ; ++j) {
+      Raw<V, WT>::abs(q0[j], a0[j]);
+      Raw<V, WT>::abs(q1[j], a1[j]);
+      float x[V];
+#pragma unroll
+      for (int e = 0; e < V; e += 4) {
+        const float4 t = reinterpret_cast<const float4*>(vs)[(ec[j] + e) >> 2];
+        x[e] = t.x; x[e + 1] = t.y; x[e + 2] = t.z; x[e + 3] = t.w;
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        s0 += ok[j] ? a0[j][e] * x[e] : 0.f;
+        s1 += ok[j] ? a1[j][e] * x[e] : 0.f;
+      }
+    }
+    const float u0 = wave_sum(s0) / vnorm, u1 = wave_sum(s1) / vnorm;
+    const float m0 = r < re ? u0 : 0.f, m1 = r + 1 < re ? u1 : 0.f;
+    // Every lane stores the (wave-uniform) values, rows past re into the sink
+    // slot: no branch around a store (its join would wait for every load in
+    // flight, the prefetched rows included).
+    *(r < re ? u + r : sink) = u0;
+    *(r + 1 < re ? u + r + 1 : sink) = u1;
+    usq += m0 * m0;
+    usq += m1 * m1;
+#pragma unroll
+    for (int j = 0; j < SV_FJ; ++j)
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        cp[j][e] += a0[j][e] * m0;
+        cp[j][e] += a1[j][e] * m1;
+      }
+  };
+  // Wave w takes rows rb + 2w + 8i and the next, two at a time, the next
+  // two already loading.  Both halves of a step are unconditional (rows past
+  // re are masked inside process).
+  RT qa0[SV_FJ], qa1[SV_FJ], qb0[SV_FJ], qb1[SV_FJ];
+  int64_t r = rb + 2 * wave;
+  load(r, qa0);
+  load(r + 1, qa1);
+  for (; r < re; r += 16) {   // uniform per wave
+    load(r + 8, qb0);
+    load(r + 9, qb1);
+    process(r, qa0, qa1);
+    load(r + 16, qa0);
+    load(r + 17, qa1);
+    process(r + 8, qb0, qb1);
+  }
+  // Column sums of the four waves, added in wave order.
+#pragma unroll
+  for (int j = 0; j < SV_FJ; ++j)
+#pragma unroll
+    for (int e = 0; e < V; e += 4)
+      reinterpret_cast<float4*>(cs[wave])[((64 * j + lane) * V + e) >> 2] =
+          float4{cp[j][e], cp[j][e + 1], cp[j][e + 2], cp[j][e + 3]};
+  if (lane == 0) usw[wave] = usq;
+  __syncthreads();
+  for (int k = tid; k < K; k += 256)
+    part[(int64_t)blockIdx.x * K + k] = ((cs[0][k] + cs[1][k]) + cs[2][k]) + cs[3][k];
+  if (tid == 0) upart[blockIdx.x] = ((usw[0] + usw[1]) + usw[2]) + usw[3];
+}
+
 // ---------------------------------------------------------------- column reduction
 // v[k] = Σ_c part[c][k] / ||u||, ||u||^2 = Σ_b upart[b].  Workgroup = SV_RCOLS
 // columns: thread (l, q) sums chunks l, l + SV_CLANES, ... of columns
@@ -328,14 +449,26 @@ struct Layout {
   float *part, *v, *u, *upart;
 };
 
-// Workspace: part [chunks][K] first (16-byte aligned rows, K % 4 == 0), then
-// v [K], u [N], upart [nub].
+// Fused pass: rows per workgroup, so that the grid is one workgroup per CU
+// (256 on MI355X) and its partial rows stay small (K floats each).
+constexpr int64_t SV_FUSED_BLOCKS = 256;
+inline int64_t fused_rpw(int64_t N) {
+  const int64_t r = (N + SV_FUSED_BLOCKS - 1) / SV_FUSED_BLOCKS;
+  return r < SV_RPB ? SV_RPB : r;
+}
+inline int64_t part_rows(int64_t N) {   // partial rows of the column pass or of the fused pass
+  const int64_t c = (N + SV_CHUNK - 1) / SV_CHUNK, f = (N + fused_rpw(N) - 1) / fused_rpw(N);
+  return c > f ? c : f;
+}
+
+// Workspace: part [part_rows][K] first (16-byte aligned rows, K % 4 == 0), then
+// v [K], u [N], upart [nub], then slack (the fused pass's sink slot).
 Layout layout(float* ws, int64_t N, int64_t K) {
   Layout L;
   L.chunks = (N + SV_CHUNK - 1) / SV_CHUNK;
   L.nub = (N + SV_RPB - 1) / SV_RPB;
   L.part = ws;
-  L.v = L.part + L.chunks * K;
+  L.v = L.part + part_rows(N) * K;
   L.u = L.v + K;
   L.upart = L.u + N;
   return L;
@@ -348,7 +481,19 @@ hipError_t run(const WT* W, int64_t N, int64_t K, int iters, void* av, void* bv,
   const dim3 gc((unsigned)((K / CV + 255) / 256), (unsigned)L.chunks);
   const dim3 gv((unsigned)((K + SV_RCOLS - 1) / SV_RCOLS));
   hipLaunchKernelGGL(svid_init_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, L.v, K);
+  // Rows of at most 512·V elements (16-byte loads) take the fused pass: one
+  // read of W per iteration instead of two.
+  const bool fused = V > 1 && K <= 64 * SV_FJ * V;
+  const int64_t rpw = fused_rpw(N), nf = (N + rpw - 1) / rpw;
   for (int it = 0; it < iters; ++it) {
+    if constexpr (V > 1) {
+      if (fused) {
+        hipLaunchKernelGGL((svid_fused_kernel<WT, V>), dim3((unsigned)nf), dim3(256), 0, st, W, N, K, rpw, L.v, L.u,
+                           L.upart, L.part, L.upart + L.nub);
+        hipLaunchKernelGGL(svid_vreduce_kernel, gv, dim3(256), 0, st, L.part, nf, K, L.upart, nf, L.v);
+        continue;
+      }
+    }
     hipLaunchKernelGGL((svid_rows_kernel<WT, V>), gr, dim3(256), 0, st, W, N, K, L.v, L.u, L.upart);
     hipLaunchKernelGGL((svid_cols_kernel<WT, CV>), gc, dim3(256), 0, st, W, N, K, L.u, L.part);
     hipLaunchKernelGGL(svid_vreduce_kernel, gv, dim3(256), 0, st, L.part, L.chunks, K, L.upart, L.nub, L.v);
@@ -380,8 +525,8 @@ hipError_t run_s(int scale_dtype, const void* W, int64_t N, int64_t K, int iters
 }  // namespace
 
 size_t svid_workspace_floats(int64_t N, int64_t K) {
-  const int64_t chunks = (N + SV_CHUNK - 1) / SV_CHUNK, nub = (N + SV_RPB - 1) / SV_RPB;
-  return (size_t)(chunks * K + K + N + nub + 64);
+  const int64_t nub = (N + SV_RPB - 1) / SV_RPB;
+  return (size_t)(part_rows(N) * K + K + N + nub + 64);
 }
 
 hipError_t launch_svid(const void* W, int w_dtype, int64_t N, int64_t K, int iters, void* a, void* b,

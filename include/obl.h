@@ -153,7 +153,8 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
  *   |W|: σ1 u1 v1^T of its leading singular triple, split as a = sqrt(σ1) u1,
  *   b = sqrt(σ1) v1 with the (nonnegative) singular vectors of |W|.
  *   W       [N][K] dense, w_dtype OBL_F32, OBL_F16 or OBL_BF16, device.
- *   iters   power-iteration steps (each reads |W| twice); >= 1.
+ *   iters   power-iteration steps, >= 1; each reads |W| once (K <= 4096 with
+ *           16-bit W, K <= 2048 with fp32 W, W 16-byte aligned) or twice.
  *   packed  [N][K/32] Sign(W) (format above; 0 and -0 pack as +1), written.
  *   a [N], b [K] scale_dtype (OBL_F32 or OBL_F16), written.
  *   Uses the library's per-device scratch (see Ownership); sums are fp32 in a
