@@ -290,19 +290,20 @@ void svid_fused_kernel(const WT* __restrict__ W, int64_t N, int64_t K, int64_t r
     const int f = (256 * i + tid) * 4;
     const bool okv = f < K;
     const float4 t = *reinterpret_cast<const float4*>(v + (okv ? f : 0));
-    reinterpret_cast<float4*>(vs)[f >> 2] = t;
+    // Zeros past K: the dot products below then need no mask (|w| · 0).
+    reinterpret_cast<float4*>(vs)[f >> 2] = okv ? t : float4{0.f, 0.f, 0.f, 0.f};
     vsq += okv ? ((t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w)) : 0.f;
   }
   const float vnorm = sqrtf(block_sum(vsq, red));   // its barrier also publishes vs
 
   const int64_t rb = (int64_t)blockIdx.x * rpw, re = min(rb + rpw, N);
+  // Weight loads past K re-read the last V columns (in bounds, finite); the
+  // products use the unclamped column, whose v slot past K is zero.
   int ec[SV_FJ];
-  bool ok[SV_FJ];
 #pragma unroll
   for (int j = 0; j < SV_FJ; ++j) {
     const int e = (64 * j + lane) * V;
-    ok[j] = e < K;
-    ec[j] = ok[j] ? e : (int)K - V;
+    ec[j] = e < K ? e : (int)K - V;
   }
   auto load = [&](int64_t r, RT (&q)[SV_FJ]) {   // rows past N re-read row N - 1 (unused)
     const WT* w = W + min(r, N - 1) * K;
@@ -326,13 +327,13 @@ void svid_fused_kernel(const WT* __restrict__ W, int64_t N, int64_t K, int64_t r
       float x[V];
 #pragma unroll
       for (int e = 0; e < V; e += 4) {
-        const float4 t = reinterpret_cast<const float4*>(vs)[(ec[j] + e) >> 2];
+        const float4 t = reinterpret_cast<const float4*>(vs)[((64 * j + lane) * V + e) >> 2];
         x[e] = t.x; x[e + 1] = t.y; x[e + 2] = t.z; x[e + 3] = t.w;
       }
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        s0 += ok[j] ? a0[j][e] * x[e] : 0.f;
-        s1 += ok[j] ? a1[j][e] * x[e] : 0.f;
+      for (int e = 0; e < V; ++e) {   // columns past K meet v = 0
+        s0 += a0[j][e] * x[e];
+        s1 += a1[j][e] * x[e];
       }
     }
     const float u0 = wave_sum(s0) / vnorm, u1 = wave_sum(s1) / vnorm;
