@@ -559,7 +559,16 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     // otherwise the four lanes of a column load all four quads.  Quads past
     // the end re-read quad 0 (masked below).
     u32x4 wq[SL ? 1 : CPW][4];
-    if constexpr (SL) {
+    if constexpr (SL && PER <= 4) {
+      // Up to 16 rows: the sign words marked non-temporal, which keeps the X
+      // rows that every workgroup reads in L2.  Measured both ways: 16 x 4096
+      // x 4096 5.67 -> 5.43 us, 4 x 4096 x 4096 5.15 -> 4.80, DBF decode 11.0
+      // -> 10.7; 32 rows (and the register-staged signs below) measured 1-3 %
+      // slower with it.  The choice is by template: a branch around the DMAs
+      // made the compiler wait for every transfer at its join.
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) dma16_nt(wr, sg + 64 * c, so[c], (uint32_t)(step0 * 4));
+    } else if constexpr (SL) {
 #pragma unroll
       for (int c = 0; c < CPW; ++c) dma16(wr, sg + 64 * c, so[c], (uint32_t)(step0 * 4));
     } else {

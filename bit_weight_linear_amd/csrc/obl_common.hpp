@@ -85,6 +85,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_wave_b
                                            (int)voff, (int)soff, 0, 0);
 }
 
+// The same, marked non-temporal (streamed data that no later access reuses:
+// it does not displace cached operands).
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff,
+                                         uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)voff, (int)soff, 0, 2);
+}
+
 // Workgroup barrier that makes this wave's LDS writes visible but does not
 // wait for its global loads in flight (__syncthreads() also drains vmcnt).
 // s_waitcnt immediate: lgkmcnt = 0, vmcnt = 63 and expcnt = 7 (no wait).
