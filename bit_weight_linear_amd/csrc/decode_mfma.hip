@@ -447,7 +447,7 @@ __device__ __forceinline__ void wk_wave_sync() {
 // backward (bf16 gin): gsum[n] = Σ_m gin[m][n] · y[m][n] over the block's
 // rows in order, and, with gout, gout[m][n] = y[m][n] · gscale[n] (fp32 or
 // bf16 as gout_bf16 says).
-template <int XM, typename ST, typename YT, int CPW, int PER>
+template <int XM, typename ST, typename YT, int CPW, int PER, bool NT>
 __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3,
@@ -559,13 +559,15 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     // otherwise the four lanes of a column load all four quads.  Quads past
     // the end re-read quad 0 (masked below).
     u32x4 wq[SL ? 1 : CPW][4];
-    if constexpr (SL && PER <= 4) {
+    if constexpr (SL && PER <= 4 && NT) {
       // Up to 16 rows: the sign words marked non-temporal, which keeps the X
       // rows that every workgroup reads in L2.  Measured both ways: 16 x 4096
       // x 4096 5.67 -> 5.43 us, 4 x 4096 x 4096 5.15 -> 4.80, DBF decode 11.0
       // -> 10.7; 32 rows (and the register-staged signs below) measured 1-3 %
       // slower with it.  The choice is by template: a branch around the DMAs
-      // made the compiler wait for every transfer at its join.
+      // made the compiler wait for every transfer at its join.  NT = false
+      // for the backward's contractions (gradient epilogue): they follow the
+      // forward over the same weights, which plain loads may find cached.
 #pragma unroll
       for (int c = 0; c < CPW; ++c) dma16_nt(wr, sg + 64 * c, so[c], (uint32_t)(step0 * 4));
     } else if constexpr (SL) {
@@ -736,11 +738,14 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
   }
 }
 
-template <int XM, typename ST, typename YT, int CPW, int PER>
+template <int XM, typename ST, typename YT, int CPW, int PER, bool NT = true>
 hipError_t launch_wk(const LinearArgs& a) {
+  if constexpr (XM == WK_B2 && NT) {
+    if (a.gsum) return launch_wk<XM, ST, YT, CPW, PER, false>(a);   // the backward's contractions
+  }
   const int64_t blocks = (a.N + 16 * CPW - 1) / (16 * CPW);
   if (blocks > 0x7fffffff || a.M > 4 * PER) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_wk_kernel<XM, ST, YT, CPW, PER>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((decode_wk_kernel<XM, ST, YT, CPW, PER, NT>), dim3((unsigned)blocks),
                      dim3(64 * wk_waves(XM, PER, CPW)), wk_lds_bytes(XM, PER, CPW), a.stream,
                      static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N, static_cast<const f16_t*>(a.pre),
                      static_cast<const ST*>(a.post), static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.T3),
