@@ -49,8 +49,6 @@
 // them at bits 15 and 31 and one v_bitop3 applies them to the magnitudes.
 // The contraction takes four steps at a time: all LDS reads of the four are
 // issued before the first MFMA and each step owns its accumulators.
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "obl_common.hpp"
@@ -345,17 +343,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   // Slices in batches of 8 (clamped indexes, masked terms): every load of a
   // batch is in flight together, also for slice counts that are not a multiple
   // of 8 (a plain tail loop would wait once per slice).
-  float acc = 0.f;
+  // The slices' sums are added in slice order with compensated (Kahan)
+  // summation: the error stays that of one slice plus about two roundings
+  // however many slices K spans.
+  float acc = 0.f, comp = 0.f;
   for (int s0 = 0; s0 < nslices; s0 += 8) {
     float v[8];
-    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partials[(int64_t)(s0 + u < nslices ? s0 + u : 0) * MN + e];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      ok[u] = s0 + u < nslices;
-      v[u] = partials[(int64_t)(ok[u] ? s0 + u : 0) * MN + e];
+      if (s0 + u < nslices) {   // uniform over the grid
+        const float y = v[u] - comp;
+        const float t = acc + y;
+        comp = (t - acc) - y;
+        acc = t;
+      }
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += ok[u] ? v[u] : 0.f;
   }
   Store<YT>::put(&Y[e], acc * s);
 }
@@ -550,7 +554,40 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
 #pragma unroll
         for (int a = 0; a < NA; ++a) acc[u][c][f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A wave's slices: the sum over one slice (terms of a set, then the sets in
+  // order) is added into a running total with compensated (Kahan) summation,
+  // so a lane's rounding error is that of one slice plus about two roundings
+  // however many slices it takes; with one slice per wave (K <= 4096) the
+  // total is that slice's sum exactly.
+  f32x4 ktot[CPW][RF], kcomp[CPW][RF];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int f = 0; f < RF; ++f) ktot[c][f] = kcomp[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fold_slice = [&]() {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        f32x4 sl = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < AU; ++u) {
+          f32x4 su = acc[u][c][f][0];
+#pragma unroll
+          for (int a = 1; a < NA; ++a) su = su + acc[u][c][f][a];
+          sl = sl + su;
+#pragma unroll
+          for (int a = 0; a < NA; ++a) acc[u][c][f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const f32x4 y = sl - kcomp[c][f];
+        const f32x4 t = ktot[c][f] + y;
+        kcomp[c][f] = (t - ktot[c][f]) - y;
+        ktot[c][f] = t;
+      }
+  };
+
   for (int s = wave; s < nslices; s += WAVES) {
+    if (s != wave) fold_slice();   // uniform: the previous slice's sums into the total
     const int64_t step0 = (int64_t)s * DEC_STEPS;
     const int64_t k0 = step0 * 32;
     const int nsteps = (int)min((int64_t)DEC_STEPS, kw - step0);   // a multiple of 4
@@ -675,21 +712,9 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     wk_wave_sync();   // the next slice's DMAs overwrite this slice's LDS
   }
 
-  // Fixed summation order: terms of a set, then the sets in order.
-  f32x4 tot[CPW][RF];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c)
-#pragma unroll
-    for (int f = 0; f < RF; ++f) {
-      tot[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < AU; ++u) {
-        f32x4 su = acc[u][c][f][0];
-#pragma unroll
-        for (int a = 1; a < NA; ++a) su = su + acc[u][c][f][a];
-        tot[c][f] = tot[c][f] + su;
-      }
-    }
+  // The last slice (or zeros for a wave without one) into the total.
+  fold_slice();
+  const f32x4 (&tot)[CPW][RF] = ktot;
   // Waves' sums through LDS: red[wave][row][column]; lane holds rows
   // 16f + 4g .. +3 of column 16c + j.  Added in wave order.
   __syncthreads();   // every wave is done with its staging region
@@ -707,9 +732,17 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const int o = tid + THREADS * r;
     const int m = o / NC, cl = o - (o / NC) * NC;
     if (o < 16 * RF * NC && m < M && n0 + cl < N) {
-      float v = 0.f;
+      // The waves' totals in wave order, compensated (Kahan) as the slices
+      // within a wave: with one slice per wave this is the split kernel's
+      // slice reduction, term for term.
+      float v = 0.f, vc = 0.f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) v += red[(w * 16 * RF + m) * RS + cl];
+      for (int w = 0; w < WAVES; ++w) {
+        const float y = red[(w * 16 * RF + m) * RS + cl] - vc;
+        const float t = v + y;
+        vc = (t - v) - y;
+        v = t;
+      }
       const float y = v * post_o[r];
       const int64_t e = (int64_t)m * N + n0 + cl;
       Store<YT>::put(&Y[e], y);
@@ -766,13 +799,12 @@ hipError_t launch_wk_rows(const LinearArgs& a) {
   return hipErrorInvalidValue;   // WK_T3 serves up to 8 rows
 }
 
-// Columns per wave of the whole-K variant, or 0 for the split kernel.
-// OBL_DECODE=split|wk1|wk2|wk4 forces a choice (tests cover each).
+// Columns per wave of the whole-K variant, or 0 for the split kernel.  The
+// test suite can force either (forced_kernels().decode).
 int wk_columns_per_wave(const LinearArgs& a, const DeviceInfo& dev) {
-  const char* e = std::getenv("OBL_DECODE");
-  if (e && !std::strcmp(e, "split")) return 0;
-  int cpw = 0;
-  if (e && e[0] == 'w' && e[1] == 'k' && (e[2] == '1' || e[2] == '2' || e[2] == '4') && !e[3]) cpw = e[2] - '0';
+  const int forced = forced_kernels().decode;
+  if (forced == 1) return 0;
+  int cpw = forced > 10 ? forced - 10 : 0;
   if (cpw == 0) {
     // Default: the fewest columns per wave that keep the grid within one
     // workgroup per CU (the 16-row staging takes most of a CU's LDS, so a
@@ -806,15 +838,18 @@ hipError_t launch_wk_any(const LinearArgs& a, int cpw) {
   return launch_wk_rows<XM, ST, YT, 1>(a);
 }
 
+// K-slices of the split kernel.
+int64_t split_slices(const LinearArgs& a) { return (a.K / 32 + DEC_STEPS - 1) / DEC_STEPS; }
+
 template <int MODE, typename XT, typename ST, typename YT, bool PRE>
 hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
   const int64_t kw = a.K / 32;
   const int64_t tiles = (a.N + DEC_BN - 1) / DEC_BN;
-  const int64_t nslices = (kw + DEC_STEPS - 1) / DEC_STEPS;
-  Scratch sc{};
+  const int64_t nslices = split_slices(a);
+  float* partials = nullptr;
   if (nslices > 1) {
-    hipError_t e = scratch_reserve(dev.device, (size_t)(nslices * a.M * a.N), &sc);
-    if (e != hipSuccess) return e;
+    partials = a.sx ? a.sx->get(0, (size_t)(nslices * a.M * a.N)) : nullptr;
+    if (!partials) return hipErrorInvalidValue;
   }
   const bool fast = (kw % 4 == 0) && (reinterpret_cast<uintptr_t>(a.W) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(a.X) % 16 == 0);
@@ -827,17 +862,28 @@ hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
   if (fast)
     hipLaunchKernelGGL((decode_mfma_kernel<MODE, XT, ST, YT, PRE, true>), dim3((unsigned)blocks),
                        dim3(DEC_THREADS), 0, a.stream, X, (int)a.M, a.K, a.W, a.N, pre, post, Y,
-                       (int)nslices, sc.partials);
+                       (int)nslices, partials);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<MODE, XT, ST, YT, PRE, false>), dim3((unsigned)blocks),
                        dim3(DEC_THREADS), 0, a.stream, X, (int)a.M, a.K, a.W, a.N, pre, post, Y,
-                       (int)nslices, sc.partials);
+                       (int)nslices, partials);
   if (nslices > 1) {
     const int64_t MN = a.M * a.N;
     hipLaunchKernelGGL((splitk_reduce_kernel<ST, YT>), dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
-                       a.stream, sc.partials, (int)nslices, MN, a.N, post, Y);
+                       a.stream, partials, (int)nslices, MN, a.N, post, Y);
   }
   return hipGetLastError();
+}
+
+// Whether the call runs on the whole-K kernel in mode B2 (bf16 x with an fp16
+// input-side scale, aligned; every public entry point passes an input-side
+// scale, so only this mode reaches it), and with how many column groups per
+// wave; 0 for the split kernel.
+int wk_b2_columns(const LinearArgs& a, const DeviceInfo& dev) {
+  const bool b2 = a.x_dtype == DT_BF16 && a.pre && a.scale_dtype == DT_F16;
+  if (!wk_eligible(a, b2)) return 0;
+  const int cpw = wk_columns_per_wave(a, dev);
+  return (cpw > 0 && (!a.T3 || a.y_dtype == DT_F32)) ? cpw : 0;
 }
 
 template <typename ST, typename YT>
@@ -845,8 +891,6 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
   // bf16 x: A is x itself (any alignment: the staging copies it to LDS).
   const bool raw = a.x_dtype == DT_BF16;
   const bool b1 = raw && !a.pre, b2 = raw && a.pre && a.scale_dtype == DT_F16;
-  // (Every public entry point passes an input-side scale, so only mode B2
-  // reaches the whole-K variant.)
   if (a.x_dtype == DT_BF16X3) {
     // Exact bf16 terms of an fp32 input (DBF stage 2): the whole-K kernel only.
     const int cpw = wk_columns_per_wave(a, dev);
@@ -854,10 +898,8 @@ hipError_t launch_mode(const LinearArgs& a, const DeviceInfo& dev) {
     return launch_wk_any<WK_T3, ST, YT>(a, cpw);
   }
   if constexpr (std::is_same<ST, f16_t>::value) {
-    if (wk_eligible(a, b2)) {
-      const int cpw = wk_columns_per_wave(a, dev);
-      if (cpw > 0 && (!a.T3 || std::is_same<YT, float>::value)) return launch_wk_any<WK_B2, ST, YT>(a, cpw);
-    }
+    const int cpw = wk_b2_columns(a, dev);
+    if (cpw > 0) return launch_wk_any<WK_B2, ST, YT>(a, cpw);
   }
   if (a.T3 || a.gsum || a.gout) return hipErrorInvalidValue;   // epilogues of the whole-K kernel only
   if (a.M > kDecodeMaxM) return hipErrorInvalidValue;   // the split kernel stages 16 rows
@@ -900,10 +942,15 @@ bool decode_terms_ok(const LinearArgs& s1, const LinearArgs& s2) {
 
 bool decode_wide_ok(const LinearArgs& a) {
   const bool b2 = a.x_dtype == DT_BF16 && a.pre && a.scale_dtype == DT_F16;
-  const char* e = std::getenv("OBL_DECODE");
   // (Y2, the bf16 copy of the output for a DBF prefill stage, is written by
   // the prefill GEMM only.)
-  return a.M >= 1 && a.M <= kDecodeWideMaxM && !a.Y2 && wk_eligible(a, b2) && !(e && !std::strcmp(e, "split"));
+  return a.M >= 1 && a.M <= kDecodeWideMaxM && !a.Y2 && wk_eligible(a, b2) && forced_kernels().decode != 1;
+}
+
+void decode_scratch(const LinearArgs& a, const DeviceInfo& dev, ScratchNeed* need) {
+  if (a.x_dtype == DT_BF16X3 || wk_b2_columns(a, dev) > 0) return;   // the whole-K kernel: none
+  const int64_t nslices = split_slices(a);
+  if (nslices > 1) need->need(0, (size_t)(nslices * a.M * a.N));
 }
 
 }  // namespace obl

@@ -24,7 +24,6 @@
 // exactly two per CU on 256 CUs.  Workgroups are dispatched round-robin over
 // the 8 XCDs, so the tile order puts all tiles of one block-row on one XCD:
 // that XCD's L2 then holds the shared activation rows.
-#include <cstdlib>
 #include <type_traits>
 
 #include "obl_common.hpp"
@@ -549,11 +548,11 @@ hipError_t launch_t(const LinearArgs& a, const DeviceInfo&) {
   return hipGetLastError();
 }
 
-// OBL_GEMM=v1 / v2 force the 8-wave / the LDS-staged kernel (tests compare
-// them with the default choice).
+// The test suite can force the 8-wave or the LDS-staged kernel
+// (forced_kernels().gemm 1 / 2) to compare them with the default choice.
 int gemm_forced() {
-  const char* e = std::getenv("OBL_GEMM");
-  return (e && e[0] == 'v' && (e[1] == '1' || e[1] == '2')) ? e[1] - '0' : 0;
+  const int f = forced_kernels().gemm;
+  return (f == 1 || f == 2) ? f : 0;
 }
 
 template <typename ST, typename YT>
@@ -590,6 +589,14 @@ hipError_t launch_y(const LinearArgs& a, const DeviceInfo& dev) {
 }
 
 }  // namespace
+
+void gemm_scratch(const LinearArgs& a, const DeviceInfo& dev, ScratchNeed* need) {
+  // The same order of choices as launch_mode: only the main kernel (split K)
+  // and its prescaled route use scratch.
+  if (gemm_forced() != 0) return;
+  if (gemm_wide_eligible(a)) gemm_wide_scratch(a, dev, need);
+  else if (gemm_wide_prescale_eligible(a)) gemm_wide_prescaled_scratch(a, dev, need);
+}
 
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev) {
   return a.scale_dtype == DT_F32 ? launch_y<float>(a, dev) : launch_y<f16_t>(a, dev);

@@ -64,7 +64,6 @@
 //    the reduction reading them back; more slices of fewer stages stop
 //    paying at about 8.
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "obl_common.hpp"
@@ -556,6 +555,13 @@ int split_count(int64_t tiles, int64_t nk, int num_cus) {
   return (int)std::max<int64_t>(s, 1);
 }
 
+// K-slices of a grid of `tiles` tiles (1: no split) and k-stages per slice.
+int split_plan(int64_t tiles, int64_t nk, int num_cus, int* per) {
+  int nsplit = split_count(tiles, nk, num_cus);
+  *per = (int)((nk + nsplit - 1) / nsplit);
+  return (int)((nk + *per - 1) / *per);                     // every slice non-empty
+}
+
 template <typename ST, typename YT, bool PRE, int FN, int WR>
 hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
   constexpr int BN = GwTile<FN, WR>::BN, BM = GwTile<FN, WR>::BM;
@@ -564,13 +570,11 @@ hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
   const int64_t tiles = mt * nt;
   const int64_t nk = a.K / GW_KT;
   const size_t lds = (PRE ? gw_btab_entries(a.K) : 0) * sizeof(uint32_t);
-  int nsplit = split_count(tiles, nk, dev.num_cus);
+  int per = 0;
+  const int nsplit = split_plan(tiles, nk, dev.num_cus, &per);
   if (nsplit > 1) {
-    const int per = (int)((nk + nsplit - 1) / nsplit);
-    nsplit = (int)((nk + per - 1) / per);                   // every slice non-empty
-    float* part = nullptr;
-    hipError_t e = split_reserve(dev.device, (size_t)nsplit * (size_t)(a.M * a.N), &part);
-    if (e != hipSuccess) return e;
+    float* part = a.sx ? a.sx->get(1, (size_t)nsplit * (size_t)(a.M * a.N)) : nullptr;
+    if (!part) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_wide_kernel<ST, float, PRE, true, FN, WR>), dim3((unsigned)(tiles * nsplit)),
                        dim3(GW_THREADS), lds, a.stream, static_cast<const bf16_t*>(a.X), a.M, a.K, a.W, a.N,
                        static_cast<const ST*>(a.pre), static_cast<const ST*>(a.post), nullptr, nullptr, (int)mt,
@@ -608,7 +612,7 @@ hipError_t launch_fn(const LinearArgs& a, const DeviceInfo& dev) {
 // per-column cost of the 256-wide tile against the 448-wide one.  Measured at
 // M = 2048, K = 4096: N = 14336 keeps 448 (217 vs 245 us), N = 11008 and
 // N = 4096 take 256 (182 vs 198 us, 67 vs 96 us; the 128-wide tile 77 us).
-// OBL_GEMM=w1 / w2 / w4 / w7 forces a tile (tests).
+// The test suite can force a tile (forced_kernels().gemm 11 / 12 / 14 / 17).
 int64_t rounds(int64_t M, int64_t N, int bn, int cus) {
   const int64_t tiles = ((M + 127) / 128) * ((N + bn - 1) / bn);
   return (tiles + cus - 1) / cus;
@@ -616,11 +620,8 @@ int64_t rounds(int64_t M, int64_t N, int bn, int cus) {
 
 // Returns FN for the 128-row tiles, or 1 for the 64 x 128 tile (WR = 1).
 int pick_fn(int64_t M, int64_t N, int cus) {
-  const char* e = std::getenv("OBL_GEMM");
-  if (e && e[0] == 'w' && e[1] == '1') return 1;
-  if (e && e[0] == 'w' && e[1] == '2') return 2;
-  if (e && e[0] == 'w' && e[1] == '4') return 4;
-  if (e && e[0] == 'w' && e[1] == '7') return 7;
+  const int forced = forced_kernels().gemm;
+  if (forced == 11 || forced == 12 || forced == 14 || forced == 17) return forced - 10;
   const int64_t tiles4 = ((M + 127) / 128) * ((N + GwTile<4>::BN - 1) / GwTile<4>::BN);
   if (tiles4 * 2 <= cus) {
     const int64_t tiles1 = ((M + 63) / 64) * ((N + GwTile<1, 1>::BN - 1) / GwTile<1, 1>::BN);
@@ -717,11 +718,28 @@ bool gemm_wide_prescale_eligible(const LinearArgs& a) {
   return gemm_wide_shape_ok(a.M, a.K, a.N, false, a.W, a.W);
 }
 
+// Floats of slot 0 holding the prescaled bf16 activations.
+size_t prescaled_floats(const LinearArgs& a) { return (size_t)((a.M * a.K + 1) / 2 + 64); }
+
+void gemm_wide_scratch(const LinearArgs& a, const DeviceInfo& dev, ScratchNeed* need) {
+  const int fn = pick_fn(a.M, a.N, dev.num_cus);
+  const int bm = fn == 1 ? GwTile<1, 1>::BM : GwTile<2>::BM;
+  const int bn = fn == 1 ? GwTile<1, 1>::BN : (fn == 2 ? GwTile<2>::BN : (fn == 4 ? GwTile<4>::BN : GwTile<7>::BN));
+  const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+  int per = 0;
+  const int nsplit = split_plan(tiles, a.K / GW_KT, dev.num_cus, &per);
+  if (nsplit > 1) need->need(1, (size_t)nsplit * (size_t)(a.M * a.N));
+}
+
+void gemm_wide_prescaled_scratch(const LinearArgs& a, const DeviceInfo& dev, ScratchNeed* need) {
+  need->need(0, prescaled_floats(a));
+  gemm_wide_scratch(a, dev, need);
+}
+
 hipError_t launch_gemm_wide_prescaled(const LinearArgs& a, const DeviceInfo& dev) {
-  Scratch sc{};
-  hipError_t e = scratch_reserve(dev.device, (size_t)((a.M * a.K + 1) / 2 + 64), &sc);
-  if (e != hipSuccess) return e;
-  bf16_t* Xp = reinterpret_cast<bf16_t*>(sc.partials);
+  float* buf = a.sx ? a.sx->get(0, prescaled_floats(a)) : nullptr;
+  if (!buf) return hipErrorInvalidValue;
+  bf16_t* Xp = reinterpret_cast<bf16_t*>(buf);
   if (a.x_dtype == DT_F32) {
     if (a.scale_dtype == DT_F32) launch_prescale_p<float, float>(a, Xp);
     else launch_prescale_p<float, f16_t>(a, Xp);

@@ -117,10 +117,25 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
   }
 
+  // K > 4096 (MULTI): each slab's lookups start a fresh per-lane sum, and the
+  // slab sums are added with compensated (Kahan) summation, so a lane's error
+  // stays that of one slab's 32 adds plus about two roundings whatever K is.
+  float ktot[RPH][MR], kcomp[RPH][MR];
+#pragma unroll
+  for (int r = 0; r < RPH; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) ktot[r][m] = kcomp[r][m] = 0.f;
+
   // K <= 4096 (MULTI = false) runs the slab body once, with no loop: a loop
   // header would drain vmcnt and wait for the output-scale loads above.
   const int64_t nslab = MULTI ? K : 1;
   for (int64_t s0 = 0; s0 < nslab; s0 += LUT_SLAB_K) {
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int r = 0; r < RPH; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+    }
     // This thread's table group g (k = s0 + 4g .. +3), i.e. chunk g / 32,
     // nibble position g % 32.  Paired layout: wave w builds nibble positions
     // of parity w % 2 in chunks 4(w / 2) .. +3, so a wave's writes share one
@@ -173,10 +188,17 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
           else pr[i] = 1.f;
         }
       }
-      // Barrier without a memory wait: every wave has issued its table inputs
-      // before any wave issues sign loads, and (for later slabs) every wave has
-      // finished reading the previous table.
-      __builtin_amdgcn_s_barrier();
+      // Barrier without a wait for global loads: every wave has issued its
+      // table inputs before any wave issues sign loads.  For later slabs it
+      // also orders every wave's reads of the previous table before the
+      // writes of this one: each wave's LDS reads complete (release fence on
+      // LDS: lgkmcnt(0)) before it arrives.  Neither waits for the X/b loads
+      // just issued.
+      if (MULTI && s0 > 0) {
+        lds_barrier();
+      } else {
+        __builtin_amdgcn_s_barrier();
+      }
       load_signs();
     }
 
@@ -263,6 +285,23 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
         }
       }
     }
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int r = 0; r < RPH; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          const float y = acc[r][m] - kcomp[r][m];
+          const float t = ktot[r][m] + y;
+          kcomp[r][m] = (t - ktot[r][m]) - y;
+          ktot[r][m] = t;
+        }
+    }
+  }
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int r = 0; r < RPH; ++r)
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[r][m] = ktot[r][m];
   }
 
   // Reduce across the half-wave and write the scaled outputs.  A row index is

@@ -1,16 +1,16 @@
-// C ABI of libobl: argument validation, path dispatch and per-device scratch.
+// C ABI of libobl: argument validation, path dispatch and library scratch.
 //
 // Every check runs before the first HIP call, so a rejected call touches no
 // device state (and the error paths can be exercised without a GPU).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
-#include <cstdlib>
-#include <cstring>
+#include <functional>
 #include <initializer_list>
 #include <mutex>
-#include <new>
 #include <unordered_map>
+#include <vector>
 
 #include "../../include/obl.h"
 #include "obl_internal.hpp"
@@ -62,25 +62,24 @@ bool dims_ok(std::initializer_list<int64_t> dims) {
   return true;
 }
 
-// Path selection.  OBL_PATH=lut|decode|gemm forces a path (tests use this to
-// cover every kernel at every M it supports); unset or "auto" picks by M.
+// Path selection.  The test suite can force a path (to cover every kernel at
+// every M it supports) through obl_internal_force_kernels, for its own thread
+// only; otherwise the path follows from M.
 enum Path { P_AUTO, P_LUT, P_DECODE, P_GEMM };
+thread_local ForcedKernels t_forced;
+
 Path forced_path() {
-  const char* s = std::getenv("OBL_PATH");
-  if (!s || !*s || !std::strcmp(s, "auto")) return P_AUTO;
-  if (!std::strcmp(s, "lut")) return P_LUT;
-  if (!std::strcmp(s, "decode")) return P_DECODE;
-  if (!std::strcmp(s, "gemm")) return P_GEMM;
+  switch (t_forced.path) {
+    case 1: return P_LUT;
+    case 2: return P_DECODE;
+    case 3: return P_GEMM;
+  }
   return P_AUTO;
 }
 
-// OBL_GEMM=v1|v2 (tests forcing an older GEMM kernel, which cannot write the
-// bf16 copy of T1): keep stage 2 on the fp32 workspace.  The w* settings only
-// pick a tile width of the main kernel.
-bool gemm_forced_any() {
-  const char* e = std::getenv("OBL_GEMM");
-  return e && e[0] == 'v';
-}
+// An older GEMM kernel forced (it cannot write the bf16 copy of T1): DBF
+// stage 2 then keeps the fp32 workspace.
+bool gemm_forced_any() { return t_forced.gemm == 1 || t_forced.gemm == 2; }
 
 Path choose_path(int64_t M, obl_status* st) {
   Path p = forced_path();
@@ -95,16 +94,101 @@ Path choose_path(int64_t M, obl_status* st) {
 
 std::mutex g_mu;
 std::unordered_map<int, DeviceInfo> g_info;
-std::unordered_map<int, Scratch> g_scratch;
 
-obl_status run_linear(const LinearArgs& la, Path path) {
-  // 17..32 rows: the decode path's whole-K kernel where it takes the call and
-  // is the faster choice (fp32 contraction, one launch); otherwise the
-  // prefill GEMM.  A forced decode call it cannot take is refused.
+// The path the call actually runs: 17..32 rows take the decode path's
+// whole-K kernel where it takes the call and is the faster choice (fp32
+// contraction, one launch); a forced decode call it cannot take is refused.
+obl_status resolve_path(const LinearArgs& la, Path path, Path* out) {
   if (path == P_DECODE && la.M > kDecodeMaxM && !decode_wide_ok(la)) return OBL_ERR_SHAPE;
   if (path == P_GEMM && forced_path() == P_AUTO && decode_wide_preferred(la)) path = P_DECODE;
-  DeviceInfo dev;
-  if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+  *out = path;
+  return OBL_OK;
+}
+
+// Adds the scratch one contraction takes to `need` (the launchers carve the
+// same amounts from the reserved context).
+obl_status plan_linear(const LinearArgs& la, Path path, const DeviceInfo& dev, ScratchNeed* need) {
+  Path p = P_AUTO;
+  obl_status st = resolve_path(la, path, &p);
+  if (st != OBL_OK) return st;
+  if (p == P_DECODE) decode_scratch(la, dev, need);
+  else if (p == P_GEMM) gemm_scratch(la, dev, need);
+  return OBL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch sources.
+//
+// Pool: per device and per stream, two grow-only buffers (one per slot).
+// Keying by stream keeps calls on different streams from sharing memory;
+// calls on one stream are ordered by the stream.  A buffer that has to grow
+// is replaced, never freed: work already enqueued -- or recorded in a HIP
+// graph -- may still use it, so it stays valid until the process ends.
+// Growth needs hipMalloc, which stream capture does not allow: a call whose
+// stream is capturing and whose pool is too small returns OBL_ERR_CAPTURE
+// before anything is enqueued, and the capture stays valid.
+struct Pool {
+  float* buf[kScratchSlots] = {nullptr, nullptr};
+  size_t cap[kScratchSlots] = {0, 0};
+};
+struct PoolKey {
+  int device;
+  uintptr_t stream;
+  bool operator==(const PoolKey& o) const { return device == o.device && stream == o.stream; }
+};
+struct PoolKeyHash {
+  size_t operator()(const PoolKey& k) const { return std::hash<uintptr_t>()(k.stream) * 31u + (size_t)k.device; }
+};
+std::unordered_map<PoolKey, Pool, PoolKeyHash> g_pools;
+std::vector<float*> g_retired;                        // replaced pool buffers, kept until exit
+constexpr size_t kMinPoolFloats = size_t(1) << 20;    // 4 MiB
+
+obl_status pool_scratch(const DeviceInfo& dev, hipStream_t stream, const ScratchNeed& need, ScratchCtx* out) {
+  if (need.floats[0] == 0 && need.floats[1] == 0) return OBL_OK;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Pool& p = g_pools[PoolKey{dev.device, reinterpret_cast<uintptr_t>(stream)}];
+  for (int s = 0; s < kScratchSlots; ++s) {
+    if (need.floats[s] <= p.cap[s]) continue;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      (void)hipGetLastError();
+      return OBL_ERR_CAPTURE;
+    }
+    size_t n = std::max(need.floats[s], std::max(2 * p.cap[s], kMinPoolFloats));
+    // Relaxed capture mode for this thread while allocating, so that a
+    // capture running on another stream is not invalidated by the call.
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) return OBL_ERR_HIP;
+    float* q = nullptr;
+    const hipError_t e = hipMalloc(&q, n * sizeof(float));
+    (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return OBL_ERR_HIP;
+    }
+    if (p.buf[s]) g_retired.push_back(p.buf[s]);
+    p.buf[s] = q;
+    p.cap[s] = n;
+  }
+  for (int s = 0; s < kScratchSlots; ++s) {
+    out->base[s] = p.buf[s];
+    out->cap[s] = p.cap[s];
+  }
+  return OBL_OK;
+}
+
+enum ScratchSource { SRC_POOL };
+
+obl_status acquire_scratch(ScratchSource src, const DeviceInfo& dev, hipStream_t stream, const ScratchNeed& need,
+                           ScratchCtx* out) {
+  (void)src;
+  return pool_scratch(dev, stream, need, out);
+}
+
+// Launches one contraction whose scratch (la.sx) is already reserved.
+obl_status run_linear(const LinearArgs& la, Path path, const DeviceInfo& dev) {
+  obl_status st = resolve_path(la, path, &path);
+  if (st != OBL_OK) return st;
   hipError_t e;
   switch (path) {
     case P_LUT: e = launch_gemv_lut(la, dev); break;
@@ -114,6 +198,24 @@ obl_status run_linear(const LinearArgs& la, Path path) {
   if (e != hipSuccess) return OBL_ERR_HIP;
   if (hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
   return OBL_OK;
+}
+
+// One contraction end to end: plan its scratch, reserve it from the pool of
+// the call's stream, launch.
+obl_status plan_and_run(LinearArgs la, Path path) {
+  Path p = P_AUTO;
+  obl_status st = resolve_path(la, path, &p);   // may refuse the call: before any HIP call
+  if (st != OBL_OK) return st;
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+  ScratchNeed need;
+  st = plan_linear(la, path, dev, &need);
+  if (st != OBL_OK) return st;
+  ScratchCtx sx;
+  st = acquire_scratch(SRC_POOL, dev, la.stream, need, &sx);
+  if (st != OBL_OK) return st;
+  la.sx = &sx;
+  return run_linear(la, path, dev);
 }
 
 bool linear_dtypes_ok(obl_dtype x, obl_dtype s, obl_dtype y) {
@@ -161,47 +263,109 @@ hipError_t device_info(DeviceInfo* out) {
   return hipSuccess;
 }
 
+const ForcedKernels& forced_kernels() { return t_forced; }
+
+}  // namespace obl
+
+namespace obl {
 namespace {
-// Grow-only per-device buffer: at least 32 MiB; a larger request waits for the
-// device (work already enqueued may still use the old buffer), frees it and
-// allocates anew.  Caller holds g_mu.
-hipError_t grow(Scratch& s, size_t floats) {
-  if (s.partial_floats >= floats) return hipSuccess;
-  size_t pf = floats;
-  if (pf < (size_t(8) << 20)) pf = size_t(8) << 20;
-  if (s.partials) {
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return e;
-    (void)hipFree(s.partials);
-    s = Scratch{};
+
+// dbf_linear, parameterised by where its scratch comes from.
+obl_status dbf_impl(const void* X, obl_dtype x_dtype, int64_t M, int64_t K, const uint32_t* S2_packed, int64_t Kmid,
+                    const uint32_t* S1_packed, int64_t N, const void* b, const void* m, const void* a,
+                    obl_dtype scale_dtype, float* workspace, void* Y, obl_dtype y_dtype, void* stream,
+                    ScratchSource src) {
+  try {
+    if (M < 0 || K < 1 || Kmid < 1 || N < 1 || K % 32 != 0 || Kmid % 32 != 0 || !dims_ok({M, K, Kmid, N}))
+      return OBL_ERR_SHAPE;
+    if (!S2_packed || !S1_packed || !b || !m || !a) return OBL_ERR_NULL;
+    if (M > 0 && (!X || !Y || !workspace)) return OBL_ERR_NULL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(y_dtype))
+      return OBL_ERR_DTYPE;
+    if (!linear_dtypes_ok(x_dtype, scale_dtype, y_dtype)) return OBL_ERR_DTYPE;
+    const int xs = elem_size(x_dtype), ss = elem_size(scale_dtype), ys = elem_size(y_dtype);
+    int64_t xb = checked_bytes(M, K, xs);
+    int64_t s2b = checked_bytes(Kmid, K / 32, 4), s1b = checked_bytes(N, Kmid / 32, 4);
+    int64_t bb = checked_bytes(K, 1, ss), mb = checked_bytes(Kmid, 1, ss), ab = checked_bytes(N, 1, ss);
+    int64_t wsb = checked_bytes(M, Kmid, 4), yb = checked_bytes(M, N, ys);
+    if (xb < 0 || s2b < 0 || s1b < 0 || bb < 0 || mb < 0 || ab < 0 || wsb < 0 || yb < 0)
+      return OBL_ERR_SHAPE;
+    if ((M > 0 && !aligned(X, xs)) || !aligned(S2_packed, 4) || !aligned(S1_packed, 4) ||
+        !aligned(b, ss) || !aligned(m, ss) || !aligned(a, ss) ||
+        (M > 0 && (!aligned(workspace, 4) || !aligned(Y, ys))))
+      return OBL_ERR_ALIGN;
+    const Range ins[6] = {range_of(X, xb), range_of(S2_packed, s2b), range_of(S1_packed, s1b),
+                          range_of(b, bb), range_of(m, mb), range_of(a, ab)};
+    Range ry = range_of(Y, yb), rw = range_of(workspace, wsb);
+    for (const Range& r : ins)
+      if (overlap(ry, r) || overlap(rw, r)) return OBL_ERR_ALIAS;
+    if (overlap(ry, rw)) return OBL_ERR_ALIAS;
+    obl_status st = OBL_OK;
+    Path path = choose_path(M, &st);
+    if (st != OBL_OK) return st;
+    if (M == 0) return OBL_OK;
+    hipStream_t hs = (hipStream_t)stream;
+    // Stage 1: T1 = ((X ⊙ b) S2^T) ⊙ m, kept in fp32 in the workspace.
+    LinearArgs s1{X, x_dtype, M, K, S2_packed, Kmid, b, m, scale_dtype, workspace, OBL_F32, hs};
+    // Stage 2: Y = (T1 S1^T) ⊙ a (no input-side scale).
+    LinearArgs s2{workspace, OBL_F32, M, Kmid, S1_packed, N, nullptr, a, scale_dtype, Y, y_dtype, hs};
+    // Where stage 2 reads a copy of T1 from slot 0 of the scratch (its first
+    // t1_floats floats, 256-byte aligned), that copy's form: none, bf16, or
+    // the exact bf16 terms.  Decided from shapes and alignment alone, before
+    // the scratch exists (an aligned stand-in address for the copy).
+    const void* kAlignedStandIn = reinterpret_cast<const void*>(uintptr_t(256));
+    size_t t1_floats = 0;
+    // Prefill: the GEMM rounds T1 to bf16 for stage 2 anyway (one rounding of
+    // the input-side operand), so stage 1 also writes that bf16 copy and
+    // stage 2 reads it with the bf16 prefill kernel.
+    const bool t1_bf16 = path == P_GEMM && !gemm_forced_any() && x_dtype == OBL_BF16 &&
+                         gemm_wide_shape_ok(M, K, Kmid, true, X, S2_packed) &&
+                         gemm_wide_shape_ok(M, Kmid, N, false, kAlignedStandIn, S1_packed);
+    // Decode (up to 8 rows): stage 1 on the whole-K kernel also writes the
+    // exact bf16 terms of T1 (hi + mid + lo), and stage 2 reads those terms on
+    // the same kernel: one launch per stage, and the products stay exact.
+    const bool t1_terms = !t1_bf16 && path == P_DECODE && decode_terms_ok(s1, s2);
+    if (t1_bf16) {
+      t1_floats = scratch_round((size_t)((M * Kmid + 1) / 2));
+      s1.Y2 = const_cast<void*>(kAlignedStandIn);
+      s2.X = kAlignedStandIn;
+      s2.x_dtype = OBL_BF16;
+    } else if (t1_terms) {
+      t1_floats = scratch_round((size_t)((3 * M * Kmid + 1) / 2));
+      s1.T3 = const_cast<void*>(kAlignedStandIn);
+      s2.X = kAlignedStandIn;
+      s2.x_dtype = DT_BF16X3;
+    }
+    Path p1 = P_AUTO, p2 = P_AUTO;   // refusals before any HIP call
+    if ((st = resolve_path(s1, path, &p1)) != OBL_OK || (st = resolve_path(s2, path, &p2)) != OBL_OK) return st;
+    DeviceInfo dev;
+    if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+    // Each stage's own scratch follows the T1 copy in slot 0.
+    ScratchNeed stages;
+    if ((st = plan_linear(s1, path, dev, &stages)) != OBL_OK) return st;
+    if ((st = plan_linear(s2, path, dev, &stages)) != OBL_OK) return st;
+    ScratchNeed need = stages;
+    need.floats[0] = t1_floats + stages.floats[0];
+    ScratchCtx sx;
+    if ((st = acquire_scratch(src, dev, hs, need, &sx)) != OBL_OK) return st;
+    sx.taken[0] = t1_floats;
+    if (t1_bf16) {
+      s1.Y2 = sx.base[0];
+      s2.X = sx.base[0];
+    } else if (t1_terms) {
+      s1.T3 = sx.base[0];
+      s2.X = sx.base[0];
+    }
+    s1.sx = s2.sx = &sx;
+    st = run_linear(s1, path, dev);
+    if (st != OBL_OK) return st;
+    return run_linear(s2, path, dev);
+  } catch (...) {
+    return OBL_ERR_INTERNAL;
   }
-  float* p = nullptr;
-  hipError_t e = hipMalloc(&p, pf * sizeof(float));
-  if (e != hipSuccess) return e;
-  s = Scratch{p, pf};
-  return hipSuccess;
 }
-std::unordered_map<int, Scratch> g_split;
+
 }  // namespace
-
-hipError_t split_reserve(int device, size_t floats, float** out) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  Scratch& s = g_split[device];
-  hipError_t e = grow(s, floats);
-  if (e != hipSuccess) return e;
-  *out = s.partials;
-  return hipSuccess;
-}
-
-hipError_t scratch_reserve(int device, size_t partial_floats, Scratch* out) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  Scratch& s = g_scratch[device];
-  hipError_t e = grow(s, partial_floats);
-  if (e != hipSuccess) return e;
-  *out = s;
-  return hipSuccess;
-}
-
 }  // namespace obl
 
 using namespace obl;
@@ -219,11 +383,15 @@ const char* obl_status_string(obl_status s) {
     case OBL_ERR_HIP: return "OBL_ERR_HIP: HIP runtime error";
     case OBL_ERR_INTERNAL: return "OBL_ERR_INTERNAL: internal error";
     case OBL_ERR_VALUE: return "OBL_ERR_VALUE: scalar argument out of range";
+    case OBL_ERR_CAPTURE:
+      return "OBL_ERR_CAPTURE: the call needs more library scratch than its stream holds and the stream is "
+             "capturing; make one call of this size on that stream before capturing";
   }
   return "OBL_ERR_UNKNOWN";
 }
 
-int obl_version(void) { return 200; }  // 0.2.0: adds SVID, the backward, LayerNorm, int32 dimension limits
+// 0.3.0: per-stream scratch that is never freed, OBL_ERR_CAPTURE.
+int obl_version(void) { return 300; }
 
 obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_t K,
                           uint32_t* packed, void* stream) {
@@ -272,7 +440,7 @@ obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
     if (st != OBL_OK) return st;
     if (M == 0) return OBL_OK;
     LinearArgs la{X, x_dtype, M, K, W_packed, N, b, a, scale_dtype, Y, y_dtype, (hipStream_t)stream};
-    return run_linear(la, path);
+    return plan_and_run(la, path);
   } catch (...) {
     return OBL_ERR_INTERNAL;
   }
@@ -299,11 +467,14 @@ obl_status obl_svid(const void* W, obl_dtype w_dtype, int64_t N, int64_t K, int 
     }
     DeviceInfo dev;
     if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
-    Scratch sc{};
-    if (scratch_reserve(dev.device, svid_workspace_floats(N, K), &sc) != hipSuccess) return OBL_ERR_HIP;
     hipStream_t hs = (hipStream_t)stream;
+    ScratchNeed need;
+    need.need(0, svid_workspace_floats(N, K));
+    ScratchCtx sx;
+    obl_status st = acquire_scratch(SRC_POOL, dev, hs, need, &sx);
+    if (st != OBL_OK) return st;
     hipError_t e = launch_pack_signs(W, w_dtype, N, K, packed, hs);
-    if (e == hipSuccess) e = launch_svid(W, w_dtype, N, K, iters, a, b, scale_dtype, sc.partials, hs);
+    if (e == hipSuccess) e = launch_svid(W, w_dtype, N, K, iters, a, b, scale_dtype, sx.base[0], hs);
     if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
     return OBL_OK;
   } catch (...) {
@@ -382,7 +553,8 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
     // separate reduction launch.
     const bool auto_wide = path == P_GEMM && forced_path() == P_AUTO && decode_wide_preferred(t) &&
                            decode_wide_preferred(u);
-    if ((path == P_DECODE || auto_wide) && decode_wide_ok(t) && decode_wide_ok(u)) {
+    const bool fused = (path == P_DECODE || auto_wide) && decode_wide_ok(t) && decode_wide_ok(u);
+    if (fused) {
       t.gin = dY;
       t.gsum = da;
       u.gin = X;
@@ -390,14 +562,21 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
       u.gscale = b;
       u.gout = dX;
       u.gout_dtype = dx_dtype;
-      st = run_linear(t, path);
-      if (st != OBL_OK) return st;
-      return run_linear(u, path);
     }
-    st = run_linear(t, path);
+    Path pt = P_AUTO, pu = P_AUTO;   // refusals before any HIP call
+    if ((st = resolve_path(t, path, &pt)) != OBL_OK || (st = resolve_path(u, path, &pu)) != OBL_OK) return st;
+    DeviceInfo dev;
+    if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
+    ScratchNeed need;   // the two contractions run one after the other on the stream: one reservation serves both
+    if ((st = plan_linear(t, path, dev, &need)) != OBL_OK) return st;
+    if ((st = plan_linear(u, path, dev, &need)) != OBL_OK) return st;
+    ScratchCtx sx;
+    if ((st = acquire_scratch(SRC_POOL, dev, hs, need, &sx)) != OBL_OK) return st;
+    t.sx = u.sx = &sx;
+    st = run_linear(t, path, dev);
     if (st != OBL_OK) return st;
-    st = run_linear(u, path);
-    if (st != OBL_OK) return st;
+    st = run_linear(u, path, dev);
+    if (st != OBL_OK || fused) return st;
     hipError_t e = launch_backward_grads(x_dtype, scale_dtype, dx_dtype, dY, X, T, U, b, M, K, N, dX, da,
                                          db, hs);
     if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
@@ -464,7 +643,7 @@ obl_status obl_linear_layernorm(const void* X, obl_dtype x_dtype, int64_t M, int
     if (M == 0) return OBL_OK;
     hipStream_t hs = (hipStream_t)stream;
     LinearArgs la{X, x_dtype, M, K, W_packed, N, b, a, scale_dtype, workspace, OBL_F32, hs};
-    st = run_linear(la, path);
+    st = plan_and_run(la, path);
     if (st != OBL_OK) return st;
     hipError_t e = launch_layernorm_rows(workspace, OBL_F32, M, N, eps, gamma, beta, scale_dtype, Z, z_dtype, hs);
     if (e != hipSuccess || hipGetLastError() != hipSuccess) return OBL_ERR_HIP;
@@ -479,78 +658,19 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const uint32_t* S1_packed, int64_t N,
                       const void* b, const void* m, const void* a, obl_dtype scale_dtype,
                       float* workspace, void* Y, obl_dtype y_dtype, void* stream) {
-  try {
-    if (M < 0 || K < 1 || Kmid < 1 || N < 1 || K % 32 != 0 || Kmid % 32 != 0 || !dims_ok({M, K, Kmid, N}))
-      return OBL_ERR_SHAPE;
-    if (!S2_packed || !S1_packed || !b || !m || !a) return OBL_ERR_NULL;
-    if (M > 0 && (!X || !Y || !workspace)) return OBL_ERR_NULL;
-    if (!valid_dtype(x_dtype) || !valid_dtype(scale_dtype) || !valid_dtype(y_dtype))
-      return OBL_ERR_DTYPE;
-    if (!linear_dtypes_ok(x_dtype, scale_dtype, y_dtype)) return OBL_ERR_DTYPE;
-    const int xs = elem_size(x_dtype), ss = elem_size(scale_dtype), ys = elem_size(y_dtype);
-    int64_t xb = checked_bytes(M, K, xs);
-    int64_t s2b = checked_bytes(Kmid, K / 32, 4), s1b = checked_bytes(N, Kmid / 32, 4);
-    int64_t bb = checked_bytes(K, 1, ss), mb = checked_bytes(Kmid, 1, ss), ab = checked_bytes(N, 1, ss);
-    int64_t wsb = checked_bytes(M, Kmid, 4), yb = checked_bytes(M, N, ys);
-    if (xb < 0 || s2b < 0 || s1b < 0 || bb < 0 || mb < 0 || ab < 0 || wsb < 0 || yb < 0)
-      return OBL_ERR_SHAPE;
-    if ((M > 0 && !aligned(X, xs)) || !aligned(S2_packed, 4) || !aligned(S1_packed, 4) ||
-        !aligned(b, ss) || !aligned(m, ss) || !aligned(a, ss) ||
-        (M > 0 && (!aligned(workspace, 4) || !aligned(Y, ys))))
-      return OBL_ERR_ALIGN;
-    const Range ins[6] = {range_of(X, xb), range_of(S2_packed, s2b), range_of(S1_packed, s1b),
-                          range_of(b, bb), range_of(m, mb), range_of(a, ab)};
-    Range ry = range_of(Y, yb), rw = range_of(workspace, wsb);
-    for (const Range& r : ins)
-      if (overlap(ry, r) || overlap(rw, r)) return OBL_ERR_ALIAS;
-    if (overlap(ry, rw)) return OBL_ERR_ALIAS;
-    obl_status st = OBL_OK;
-    Path path = choose_path(M, &st);
-    if (st != OBL_OK) return st;
-    if (M == 0) return OBL_OK;
-    // Stage 1: T1 = ((X ⊙ b) S2^T) ⊙ m, kept in fp32 in the workspace.
-    LinearArgs s1{X, x_dtype, M, K, S2_packed, Kmid, b, m, scale_dtype, workspace, OBL_F32,
-                  (hipStream_t)stream};
-    // Stage 2: Y = (T1 S1^T) ⊙ a (no input-side scale).
-    LinearArgs s2{workspace, OBL_F32, M, Kmid, S1_packed, N, nullptr, a, scale_dtype, Y, y_dtype,
-                  (hipStream_t)stream};
-    // Prefill: the GEMM rounds T1 to bf16 for stage 2 anyway (one rounding of
-    // the input-side operand), so stage 1 also writes that bf16 copy into
-    // library scratch and stage 2 reads it with the bf16 prefill kernel.
-    if (path == P_GEMM && !gemm_forced_any() && x_dtype == OBL_BF16 &&
-        gemm_wide_shape_ok(M, K, Kmid, true, X, S2_packed)) {
-      DeviceInfo dev;
-      if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
-      Scratch sc{};
-      const size_t floats = (size_t)((M * Kmid + 1) / 2 + 64);
-      if (scratch_reserve(dev.device, floats, &sc) != hipSuccess) return OBL_ERR_HIP;
-      void* t1b = sc.partials;                      // hipMalloc'ed: 256-byte aligned
-      if (gemm_wide_shape_ok(M, Kmid, N, false, t1b, S1_packed)) {
-        s1.Y2 = t1b;
-        s2.X = t1b;
-        s2.x_dtype = OBL_BF16;
-      }
-    }
-    // Decode (up to 8 rows): stage 1 on the whole-K kernel also writes the
-    // exact bf16 terms of T1 (hi + mid + lo) into library scratch, and stage 2
-    // reads those terms on the same kernel: one launch per stage, and the
-    // products stay exact.
-    if (path == P_DECODE && decode_terms_ok(s1, s2)) {
-      DeviceInfo dev;
-      if (device_info(&dev) != hipSuccess) return OBL_ERR_HIP;
-      Scratch sc{};
-      const size_t floats = (size_t)((3 * M * Kmid + 1) / 2 + 64);
-      if (scratch_reserve(dev.device, floats, &sc) != hipSuccess) return OBL_ERR_HIP;
-      s1.T3 = sc.partials;
-      s2.X = sc.partials;
-      s2.x_dtype = DT_BF16X3;
-    }
-    st = run_linear(s1, path);
-    if (st != OBL_OK) return st;
-    return run_linear(s2, path);
-  } catch (...) {
-    return OBL_ERR_INTERNAL;
-  }
+  return dbf_impl(X, x_dtype, M, K, S2_packed, Kmid, S1_packed, N, b, m, a, scale_dtype, workspace, Y, y_dtype,
+                  stream, SRC_POOL);
+}
+
+// Internal export for the test suite, not declared in obl.h: forces a path
+// and kernel choice (codes in obl_internal.hpp, ForcedKernels) for the
+// calling thread's later calls; all zeros restores the automatic choice.
+// Nothing else reads or sets it, so ordinary callers always get the kernel
+// their arguments select.
+void obl_internal_force_kernels(int path, int gemm, int decode) {
+  t_forced.path = path;
+  t_forced.gemm = gemm;
+  t_forced.decode = decode;
 }
 
 }  // extern "C"

@@ -93,12 +93,16 @@ __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, void* lds_wav
                                            (int)voff, (int)soff, 0, 2);
 }
 
-// Workgroup barrier that makes this wave's LDS writes visible but does not
-// wait for its global loads in flight (__syncthreads() also drains vmcnt).
-// s_waitcnt immediate: lgkmcnt = 0, vmcnt = 63 and expcnt = 7 (no wait).
+// Workgroup barrier that orders LDS accesses across the workgroup but does
+// not wait for global loads in flight (__syncthreads() also drains vmcnt):
+// workgroup-scope release and acquire fences on LDS only (they compile to
+// lgkmcnt(0), and keep the compiler from moving LDS accesses across) around
+// s_barrier.  s_waitcnt immediate: lgkmcnt = 0, vmcnt = 63, expcnt = 7.
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // One 16x16x32 bf16 MFMA step with fp32 accumulation.

@@ -22,22 +22,28 @@
  *    stream).  Every call is asynchronous on `stream`: it returns once the work
  *    is enqueued, and buffers must stay alive until that work completes.
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer
- *    to caller memory after a call returns.  It keeps two scratch buffers per
- *    device: one for the split decode kernel's partial sums (M <= 16), the
- *    bf16 copy of the DBF intermediate at prefill sizes, the exact bf16 terms
- *    of that intermediate at decode sizes, the bf16(x ⊙ b)
- *    activations the prefill path stages for fp32 or misaligned X, and the
- *    vectors of obl_svid; one for the prefill kernel's split-K partial sums
- *    (grids with few tiles).  Each is allocated with hipMalloc on the first call that
- *    needs it (at least 32 MiB), grown when a larger one is needed (after a
- *    device synchronise) and held until process exit.  Calls that overlap in
- *    time on one device (several streams or host threads) must not both use
- *    them -- serialise them -- and the first such call must not be made
- *    inside HIP stream capture.
+ *    to caller memory after a call returns.  Some calls also use library
+ *    scratch (device memory beyond their arguments: the split decode
+ *    kernel's partial sums, a copy of the DBF intermediate, the bf16(x ⊙ b)
+ *    activations the prefill path stages for fp32 or misaligned X, the
+ *    prefill kernel's split-K partial sums on small grids, the vectors of
+ *    obl_svid).  It comes from a pool per device and per stream: calls on
+ *    different streams never share it, and calls on one stream are ordered
+ *    by the stream.  The pool grows with hipMalloc when a call needs more
+ *    than it holds; a replaced buffer is never freed (work already enqueued,
+ *    or recorded in a HIP graph, may still use it), so all pool memory is
+ *    held until the process ends.  A call that would have to grow the pool
+ *    while its stream is capturing returns OBL_ERR_CAPTURE before enqueuing
+ *    anything, and the capture stays valid: make one call of the same shape
+ *    on that stream before capturing.  A captured graph uses the scratch of
+ *    the stream it was captured on, so replays of graphs captured on one
+ *    stream must not overlap each other in time.
  *  - Errors: every argument is validated BEFORE any HIP call; a failed check
  *    returns its status and enqueues nothing.  No call aborts or throws across
  *    the ABI.  HIP failures (including launch failures seen through
- *    hipGetLastError) return OBL_ERR_HIP.
+ *    hipGetLastError) return OBL_ERR_HIP.  Every call that can use library
+ *    scratch (all but obl_pack_signs, obl_transpose_signs and obl_layernorm)
+ *    can also return OBL_ERR_CAPTURE, before enqueuing anything.
  *  - M = 0 is a valid no-op.  N, K, Kmid, rows must be >= 1 and K, Kmid must
  *    be multiples of 32 (the packed word width); a call that violates this
  *    returns OBL_ERR_SHAPE.  Every dimension must be below 2^31 and keep every
@@ -71,7 +77,8 @@ typedef OBL_ENUM(obl_status_e) {
   OBL_ERR_ALIAS = 5,    /* an output overlaps an input or another output */
   OBL_ERR_HIP = 6,      /* the HIP runtime reported an error */
   OBL_ERR_INTERNAL = 7, /* unexpected internal failure */
-  OBL_ERR_VALUE = 8     /* a scalar argument is out of range (e.g. a negative epsilon) */
+  OBL_ERR_VALUE = 8,    /* a scalar argument is out of range (e.g. a negative epsilon) */
+  OBL_ERR_CAPTURE = 9   /* library scratch would have to grow while the call's stream is capturing */
 } obl_status;
 
 typedef OBL_ENUM(obl_dtype_e) {

@@ -10,3 +10,20 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an AMD GPU (MI355X / gfx950) and the built HIP library")
+
+
+@pytest.fixture
+def forcer():
+    """forcer(path=..., gemm=..., decode=...): force kernels for the rest of the test (the library's
+    test-only hook, per thread); the automatic choice is restored at teardown."""
+    stack = []
+
+    def force(**kw):
+        from bit_weight_linear_amd import binding as B
+        cm = B.forced_kernels(**kw)
+        cm.__enter__()
+        stack.append(cm)
+
+    yield force
+    while stack:
+        stack.pop().__exit__(None, None, None)

@@ -38,18 +38,10 @@ def packed_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint32)
 
 
-@contextlib.contextmanager
 def forced_path(path):
-    old = os.environ.get("OBL_PATH")
-    if path:
-        os.environ["OBL_PATH"] = path
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("OBL_PATH", None)
-        else:
-            os.environ["OBL_PATH"] = old
+    """Force the path (None: the automatic choice) through the library's test-only hook."""
+    from bit_weight_linear_amd import binding as B
+    return B.forced_kernels(path=path)
 
 
 def path_of(M: int, path=None) -> str:

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in range(9):
+    for code in range(10):
         assert L.obl_status_string(code) != b"OBL_ERR_UNKNOWN"
     assert L.obl_status_string(99) == b"OBL_ERR_UNKNOWN"
     assert L.obl_version() >= 100
@@ -86,10 +86,10 @@ def test_linear_rejects(kw, code):
     assert lin(**kw) == code
 
 
-def test_forced_path_must_fit_m(monkeypatch):
-    monkeypatch.setenv("OBL_PATH", "lut")
+def test_forced_path_must_fit_m(forcer):
+    forcer(path="lut")
     assert lin(M=3) == b.OBL_ERR_SHAPE
-    monkeypatch.setenv("OBL_PATH", "decode")
+    forcer(path="decode")
     assert lin(M=33) == b.OBL_ERR_SHAPE
     # 17..32 rows only on the whole-K kernel (bf16 x, fp16 scales, aligned):
     # fp32 x, or a K that is not a multiple of 128, is refused before any GPU work

@@ -111,10 +111,10 @@ def test_backward_reproducible():
 
 
 @pytest.mark.parametrize("impl", ["wk1", "wk2", "wk4"])
-def test_backward_fused_epilogue_column_groups(impl, monkeypatch):
+def test_backward_fused_epilogue_column_groups(impl, forcer):
     """The gradient epilogue at every column count per wave (16, 32 and 64
     columns per workgroup), dX in bf16, against the oracle."""
-    monkeypatch.setenv("OBL_DECODE", impl)
+    forcer(decode=impl)
     M, K, N = 16, 1024, 2048
     X, dY, S, a, b = _case(M, K, N, "bf16", "f16", seed=41)
     dX, da, db, _ = _run(X, dY, S, a, b, "bf16", "f16", "bf16")

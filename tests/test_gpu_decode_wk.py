@@ -35,9 +35,9 @@ IMPLS = ["wk1", "wk2", "wk4", "split", "auto"]
 @pytest.mark.parametrize("M,K,N", WK_CASES)
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
 @pytest.mark.parametrize("impl", IMPLS)
-def test_decode_kernels_match_oracle(M, K, N, ydt, impl, monkeypatch):
+def test_decode_kernels_match_oracle(M, K, N, ydt, impl, forcer):
     G.say(f"decode {impl} M={M} K={K} N={N} y={ydt}")
-    monkeypatch.setenv("OBL_DECODE", impl)
+    forcer(decode=impl)
     c = WL.onebit_case(M, K, N, "bf16", "f16", ydt, seed=M * 7 + K + N)
     if impl == "split" and M > 16:
         # the split kernel stages 16 rows: a forced decode call is refused
@@ -68,7 +68,7 @@ def test_mid_rows_fp32_x_take_the_gemm():
 
 
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (7, 2048, 1000), (16, 640, 33)])
-def test_whole_k_one_group_is_bitwise_the_split_kernel(M, K, N, monkeypatch):
+def test_whole_k_one_group_is_bitwise_the_split_kernel(M, K, N, forcer):
     """K <= 4096 with one column group per wave adds the same fp32 terms in the
     same order as the split kernel and its slice reduction."""
     c = WL.onebit_case(M, K, N, "bf16", "f16", "f32", seed=K + N)
@@ -77,7 +77,7 @@ def test_whole_k_one_group_is_bitwise_the_split_kernel(M, K, N, monkeypatch):
     a, b = G.dev(c.a, "f16"), G.dev(c.b, "f16")
     out = {}
     for impl in ("wk1", "split"):
-        monkeypatch.setenv("OBL_DECODE", impl)
+        forcer(decode=impl)
         with G.forced_path("decode"):
             out[impl] = B.linear(X, Wp, a, b)
     torch.cuda.synchronize()
@@ -85,10 +85,10 @@ def test_whole_k_one_group_is_bitwise_the_split_kernel(M, K, N, monkeypatch):
 
 
 @pytest.mark.parametrize("impl", ["wk1", "wk2", "wk4"])
-def test_whole_k_integer_exact_and_reproducible(impl, monkeypatch):
+def test_whole_k_integer_exact_and_reproducible(impl, forcer):
     """Integer-valued inputs: every partial sum is exact in fp32, so the result
     equals the oracle exactly; repeated calls are bitwise equal."""
-    monkeypatch.setenv("OBL_DECODE", impl)
+    forcer(decode=impl)
     c = WL.onebit_case(16, 4096, 1000, "bf16", "f16", "f32", kind="int_exact", seed=3)
     X = G.dev(c.X, "bf16")
     Wp = B.pack_signs(G.signs_dev(c.W_sign))
@@ -100,10 +100,10 @@ def test_whole_k_integer_exact_and_reproducible(impl, monkeypatch):
     assert np.array_equal(G.host64(ref), O.onebit_linear(c.X, c.W_sign, c.a, c.b))
 
 
-def test_whole_k_offset_operands_use_split_kernel(monkeypatch):
+def test_whole_k_offset_operands_use_split_kernel(forcer):
     """X 2 bytes past a 16-byte boundary is not DMA-able: the call must still
     be right (the split kernel's element staging takes it)."""
-    monkeypatch.setenv("OBL_DECODE", "wk1")
+    forcer(decode="wk1")
     M, K, N = 4, 1024, 200
     c = WL.onebit_case(M, K, N, "bf16", "f16", "f32", seed=5)
     big = torch.zeros(M * K + 1, dtype=torch.bfloat16, device="cuda")
@@ -116,10 +116,10 @@ def test_whole_k_offset_operands_use_split_kernel(monkeypatch):
 
 
 @pytest.mark.parametrize("impl", ["wk1", "split"])
-def test_dbf_decode_stage1_whole_k(impl, monkeypatch):
+def test_dbf_decode_stage1_whole_k(impl, forcer):
     """DBF decode: stage 1 (bf16 x, fp16 b) runs on the kernel under test,
     stage 2 (fp32 T1) on the split kernel."""
-    monkeypatch.setenv("OBL_DECODE", impl)
+    forcer(decode=impl)
     c = WL.workload(5)
     X = G.dev(c.X, "bf16")
     S2p = B.pack_signs(G.signs_dev(c.S2))
@@ -137,13 +137,13 @@ def test_dbf_decode_stage1_whole_k(impl, monkeypatch):
 @pytest.mark.parametrize("impl", ["auto", "wk1", "wk2", "wk4"])
 @pytest.mark.parametrize("M,K,Kmid,N", [(8, 4096, 3072, 4096), (3, 1024, 640, 300), (5, 4096, 4096, 1000),
                                         (8, 512, 128, 4096)])
-def test_dbf_decode_through_exact_terms(M, K, Kmid, N, impl, monkeypatch):
+def test_dbf_decode_through_exact_terms(M, K, Kmid, N, impl, forcer):
     """Up to 8 rows with both stages on the whole-K kernel: stage 1 writes the
     exact bf16 terms (hi + mid + lo) of T1 and stage 2 contracts them against
     the signs of S1.  T1 is bitwise the single-stage result; both stages meet
     the decode tolerance against the oracle."""
     if impl != "auto":
-        monkeypatch.setenv("OBL_DECODE", impl)
+        forcer(decode=impl)
     G.say(f"dbf terms {impl} M={M} K={K} Kmid={Kmid} N={N}")
     c = WL.dbf_case(M, K, Kmid, N, seed=K + Kmid + N + M)
     X = G.dev(c.X, "bf16")

@@ -103,13 +103,13 @@ GEMM_DTYPES = [("bf16", "f16", "bf16"), ("bf16", "f16", "f32"), ("bf16", "f32", 
 @pytest.mark.parametrize("M,K,N", GEMM_CASES)
 @pytest.mark.parametrize("dts", GEMM_DTYPES, ids=lambda d: "-".join(d))
 @pytest.mark.parametrize("impl", ["auto", "w7", "w4", "w2", "w1", "v2", "v1"])
-def test_gemm_path(M, K, N, dts, impl, monkeypatch):
+def test_gemm_path(M, K, N, dts, impl, forcer):
     """impl=auto picks the main 32x32 kernel where it applies (K % 128 == 0;
     fp32 or misaligned x through the prescale pass) and its tile; w7 / w4 / w2
     force the 128-row tiles of 448 / 256 / 128 columns, w1 the 64 x 128 tile,
     v2 the LDS-staged 16x16 kernel, v1 the 8-wave kernel."""
     if impl != "auto":
-        monkeypatch.setenv("OBL_GEMM", impl)
+        forcer(gemm=impl)
     G.say(f"gemm[{impl}] M={M} K={K} N={N} {dts}")
     c = WL.onebit_case(M, K, N, *dts, seed=M + 2 * K + N)
     G.check_onebit(c, G.run_onebit(c, "gemm"), "gemm")
@@ -176,12 +176,12 @@ def test_workload4_prefill_sampled():
 
 
 @pytest.mark.parametrize("impl", ["auto", "w7"])
-def test_prefill_down_projection_sampled(impl, monkeypatch):
+def test_prefill_down_projection_sampled(impl, forcer):
     """2048 x 11008 -> 4096 (a Llama-2-7B MLP down projection): the tile-width
     choice takes 256 columns here (auto); w7 checks the 448-column tile with a
     partial last column tile.  Sampled outputs against the oracle."""
     if impl != "auto":
-        monkeypatch.setenv("OBL_GEMM", impl)
+        forcer(gemm=impl)
     c = WL.onebit_case(2048, 11008, 4096, "bf16", "f16", "bf16", seed=21)
     G.say(f"{c.name} [{impl}]")
     Y = G.run_onebit(c, "gemm")
@@ -242,12 +242,12 @@ def test_integer_exact_bitwise(path, M, K, N):
 @pytest.mark.parametrize("impl", ["w7", "w4", "w2", "w1"])
 @pytest.mark.parametrize("M,K,N", [(300, 4096, 500), (129, 640, 449), (130, 128, 500), (70, 256, 257),
                                    (513, 384, 230)])
-def test_integer_exact_gemm_tiles(M, K, N, impl, monkeypatch):
+def test_integer_exact_gemm_tiles(M, K, N, impl, forcer):
     """Every tile of the main prefill kernel, whole K over 1, 2, 3, 5 and 32
     stages (and split K where the grid is small): integer-valued inputs make
     every partial sum exact in fp32, so the result equals the oracle bit for
     bit whatever the order of accumulation."""
-    monkeypatch.setenv("OBL_GEMM", impl)
+    forcer(gemm=impl)
     G.say(f"int-exact gemm[{impl}] M={M} K={K} N={N}")
     c = WL.onebit_case(M, K, N, "bf16", "f16", "f32", kind="int_exact", seed=K + N + M)
     Y = G.run_onebit(c, "gemm")
