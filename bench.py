@@ -84,11 +84,14 @@ class Timed:
 
     def __init__(self, torch, launches):
         self.torch = torch
-        for f in launches:            # eager warm-up (allocates library scratch if any)
-            f()
+        self.stream = torch.cuda.Stream()
+        self.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            for f in launches:        # eager warm-up on the capture stream (sizes its library scratch)
+                f()
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
+        with torch.cuda.graph(self.graph, stream=self.stream):
             for f in launches:
                 f()
         torch.cuda.synchronize()

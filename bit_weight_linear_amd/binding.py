@@ -166,8 +166,8 @@ def _out(t: Optional[torch.Tensor], name: str, shape, dtypes, default_dtype, dev
 
 
 _PATHS = {None: 0, "auto": 0, "lut": 1, "decode": 2, "gemm": 3}
-_GEMMS = {None: 0, "v1": 1, "v2": 2, "w1": 11, "w2": 12, "w4": 14, "w7": 17}
-_DECODES = {None: 0, "split": 1, "wk1": 11, "wk2": 12, "wk4": 14}
+_GEMMS = {None: 0, "auto": 0, "v1": 1, "v2": 2, "w1": 11, "w2": 12, "w4": 14, "w7": 17}
+_DECODES = {None: 0, "auto": 0, "split": 1, "wk1": 11, "wk2": 12, "wk4": 14}
 
 
 _forced = threading.local()
@@ -288,7 +288,8 @@ def linear_backward(dY: torch.Tensor, X: torch.Tensor, W_packed: torch.Tensor, W
         workspace = torch.empty(M * (N + K), dtype=torch.float32, device=X.device)
     _dev(workspace, "workspace")
     _dtype(workspace, "workspace", (torch.float32,))
-    _numel(workspace, "workspace", M * (N + K))
+    if workspace.numel() < M * (N + K):
+        raise ValueError(f"workspace holds {workspace.numel()} floats, the call needs M (N + K) = {M * (N + K)}")
     dX = _out(None, "dX", (M, K), _YDT, dx_dtype, X.device)
     da = torch.empty(N, dtype=torch.float32, device=X.device)
     db = torch.empty(K, dtype=torch.float32, device=X.device)

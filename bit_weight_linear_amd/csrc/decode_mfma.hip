@@ -733,15 +733,18 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const int m = o / NC, cl = o - (o / NC) * NC;
     if (o < 16 * RF * NC && m < M && n0 + cl < N) {
       // The waves' totals in wave order, compensated (Kahan) as the slices
-      // within a wave: with one slice per wave this is the split kernel's
-      // slice reduction, term for term.
+      // within a wave, over the waves that had a slice: with at most one
+      // slice per wave this is the split kernel's slice reduction, term for
+      // term (a Kahan step that adds a zero would apply the compensation).
       float v = 0.f, vc = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        const float y = red[(w * 16 * RF + m) * RS + cl] - vc;
-        const float t = v + y;
-        vc = (t - v) - y;
-        v = t;
+        if (w < nslices) {   // uniform
+          const float y = red[(w * 16 * RF + m) * RS + cl] - vc;
+          const float t = v + y;
+          vc = (t - v) - y;
+          v = t;
+        }
       }
       const float y = v * post_o[r];
       const int64_t e = (int64_t)m * N + n0 + cl;

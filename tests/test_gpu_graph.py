@@ -22,10 +22,10 @@ def _replays_match(fn, outs):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn()                              # warm-up on the capture stream (library scratch already sized)
+        fn()                              # warm-up on the capture stream: sizes that stream's library scratch
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         fn()
     for rep in range(3):
         for o in outs:

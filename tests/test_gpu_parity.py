@@ -156,9 +156,34 @@ def test_workload3_batched_decode():
     G.say(f"  max normalised error {r:.3e}")
 
 
+def test_workload4_prefill_full():
+    """The full 2048 x 4096 x 14336 launch (bf16 output, the kernel and tile the
+    bench times) against the fp64 oracle on every one of its 29.4 M outputs, at
+    the prefill tolerance on the normalised scale."""
+    c = WL.workload(4)
+    G.say(c.name)
+    Y = G.run_onebit(c)
+    assert np.isfinite(Y).all()
+    r = G.check_onebit(c, Y)
+    G.say(f"  max normalised error over all {Y.size} outputs {r:.3e}")
+
+
+def test_workload4_shape_integer_exact_bf16():
+    """Integer-exact inputs at exactly the workload-4 shape through the default
+    prefill kernel with bf16 output: every partial sum is exact in fp32, so
+    each output must be the round-to-nearest-even bf16 of the exact value, bit
+    for bit."""
+    c = WL.onebit_case(2048, 4096, 14336, "bf16", "f16", "bf16", kind="int_exact", seed=4)
+    G.say(c.name)
+    Y = G.run_onebit(c)
+    ref = WL.round_to(O.onebit_linear(c.X, c.W_sign, c.a, c.b), "bf16")
+    bad = Y != ref
+    assert not bad.any(), f"{int(bad.sum())} outputs differ; first at {np.argwhere(bad)[0]}"
+
+
 def test_workload4_prefill_sampled():
-    """Full 2048 x 14336 x 4096 launch; the oracle computes a sample of outputs
-    one block of rows / columns at a time."""
+    """Quick check of the same launch on a sample of outputs (rows and columns at
+    the tile edges included)."""
     c = WL.workload(4)
     G.say(c.name)
     Y = G.run_onebit(c)
@@ -214,6 +239,23 @@ def test_workload5_dbf():
     r = O.max_normalised_error(Y, Y_ref, O.dbf_error_scale(c.X, c.b, c.m, c.a))
     G.say(f"  stage1 {r1:.3e} stage2 {r2:.3e} composed {r:.3e}")
     assert r1 <= G.TOL_DECODE and r2 <= G.TOL_DECODE and r <= G.TOL_DECODE
+
+
+@pytest.mark.parametrize("path,M,x_dtype,decode", [("lut", 1, "bf16", None), ("lut", 2, "bf16", None),
+                                                   ("decode", 4, "bf16", None), ("decode", 16, "bf16", None),
+                                                   ("decode", 16, "bf16", "split"), ("decode", 8, "f32", None),
+                                                   ("decode", 24, "bf16", None)])
+def test_k32768_decode_tolerance(path, M, x_dtype, decode, forcer):
+    """K = 32768 on every decode kernel (8 LUT slabs, 8 slices per whole-K wave,
+    64 split slices): the slab and slice sums are combined with compensated
+    summation, so the 1e-5 bound holds at long K too."""
+    if decode:
+        forcer(decode=decode)
+    K, N = 32768, 160
+    G.say(f"K=32768 {path} M={M} x={x_dtype} decode={decode}")
+    c = WL.onebit_case(M, K, N, x_dtype, "f16", "f32", seed=M + 33)
+    r = G.check_onebit(c, G.run_onebit(c, path), path)
+    G.say(f"  max normalised error {r:.3e}")
 
 
 @pytest.mark.parametrize("path,M", [("lut", 1), ("lut", 2), ("decode", 16), ("gemm", 64), ("gemm", 300)])
