@@ -25,11 +25,11 @@ lib = ctypes.CDLL(_LIB_PATH)
 
 # obl_status codes
 OBL_OK, OBL_ERR_NULL, OBL_ERR_SHAPE, OBL_ERR_DTYPE, OBL_ERR_ALIGN, OBL_ERR_ALIAS, OBL_ERR_HIP, \
-    OBL_ERR_INTERNAL, OBL_ERR_VALUE, OBL_ERR_CAPTURE = range(10)
+    OBL_ERR_INTERNAL, OBL_ERR_VALUE, OBL_ERR_CAPTURE, OBL_ERR_SCRATCH = range(11)
 # obl_dtype codes
 OBL_F32, OBL_F16, OBL_BF16, OBL_I8 = range(4)
 
-EXPORTS = ("obl_pack_signs", "obl_linear", "dbf_linear", "obl_transpose_signs",
+EXPORTS = ("obl_pack_signs", "obl_linear", "dbf_linear", "dbf_linear_noalloc", "obl_transpose_signs",
            "obl_linear_backward", "obl_svid", "obl_layernorm", "obl_linear_layernorm", "obl_status_string",
            "obl_version")
 
@@ -41,6 +41,8 @@ lib.obl_linear.restype = _int
 lib.dbf_linear.argtypes = [_vp, _int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _int,
                            _vp, _vp, _int, _vp]
 lib.dbf_linear.restype = _int
+lib.dbf_linear_noalloc.argtypes = lib.dbf_linear.argtypes
+lib.dbf_linear_noalloc.restype = _int
 lib.obl_transpose_signs.argtypes = [_vp, _i64, _i64, _vp, _vp]
 lib.obl_transpose_signs.restype = _int
 lib.obl_linear_backward.argtypes = [_vp, _vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _int,
@@ -254,6 +256,16 @@ def dbf_linear(X: torch.Tensor, S2_packed: torch.Tensor, S1_packed: torch.Tensor
     Returns (Y, workspace); the workspace holds T1 = ((X ⊙ b) S2^T) ⊙ m in fp32.
     """
     return _dbf(lib.dbf_linear, "dbf_linear", X, S2_packed, S1_packed, b, m, a, out_dtype, workspace, out)
+
+
+def dbf_linear_noalloc(X: torch.Tensor, S2_packed: torch.Tensor, S1_packed: torch.Tensor, b: torch.Tensor,
+                       m: torch.Tensor, a: torch.Tensor, workspace: torch.Tensor, out: torch.Tensor):
+    """``dbf_linear_noalloc``: dbf_linear whose library scratch is a fixed device array (no device
+    allocation by the library).  The caller passes the workspace and the output."""
+    if workspace is None or out is None:
+        raise ValueError("dbf_linear_noalloc takes a caller-allocated workspace and out")
+    return _dbf(lib.dbf_linear_noalloc, "dbf_linear_noalloc", X, S2_packed, S1_packed, b, m, a, out.dtype,
+                workspace, out)
 
 
 def transpose_signs(P: torch.Tensor, rows: int, K: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -177,12 +177,52 @@ obl_status pool_scratch(const DeviceInfo& dev, hipStream_t stream, const Scratch
   return OBL_OK;
 }
 
-enum ScratchSource { SRC_POOL };
+}  // namespace
+}  // namespace obl
+
+// Fixed scratch of the allocation-free entry point: a device array of
+// kFixedScratchFloats floats (64 MiB) that every GPU the library runs on
+// holds from the first such call until the process ends, split evenly into
+// the two slots.  In host code `scratch` only names the array; its device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kFixedScratchFloats = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kFixedScratchFloats];
+
+namespace obl {
+namespace {
+
+std::unordered_map<int, float*> g_fixed;   // device -> address of `scratch` there
+
+obl_status fixed_scratch(const DeviceInfo& dev, const ScratchNeed& need, ScratchCtx* out) {
+  const size_t half = kFixedScratchFloats / 2;
+  if (need.floats[0] > half || need.floats[1] > half) return OBL_ERR_SCRATCH;
+  float* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_fixed.find(dev.device);
+    if (it == g_fixed.end()) {
+      // The current device is dev.device (device_info read it just now).
+      if (hipGetSymbolAddress(reinterpret_cast<void**>(&ptr), HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        (void)hipGetLastError();
+        return OBL_ERR_HIP;
+      }
+      g_fixed.emplace(dev.device, ptr);
+    } else {
+      ptr = it->second;
+    }
+  }
+  out->base[0] = ptr;
+  out->cap[0] = half;
+  out->base[1] = ptr + half;
+  out->cap[1] = half;
+  return OBL_OK;
+}
+
+enum ScratchSource { SRC_POOL, SRC_FIXED };
 
 obl_status acquire_scratch(ScratchSource src, const DeviceInfo& dev, hipStream_t stream, const ScratchNeed& need,
                            ScratchCtx* out) {
-  (void)src;
-  return pool_scratch(dev, stream, need, out);
+  return src == SRC_FIXED ? fixed_scratch(dev, need, out) : pool_scratch(dev, stream, need, out);
 }
 
 // Launches one contraction whose scratch (la.sx) is already reserved.
@@ -270,7 +310,8 @@ const ForcedKernels& forced_kernels() { return t_forced; }
 namespace obl {
 namespace {
 
-// dbf_linear, parameterised by where its scratch comes from.
+// dbf_linear and its allocation-free variant: identical but for where their
+// scratch comes from.
 obl_status dbf_impl(const void* X, obl_dtype x_dtype, int64_t M, int64_t K, const uint32_t* S2_packed, int64_t Kmid,
                     const uint32_t* S1_packed, int64_t N, const void* b, const void* m, const void* a,
                     obl_dtype scale_dtype, float* workspace, void* Y, obl_dtype y_dtype, void* stream,
@@ -386,11 +427,13 @@ const char* obl_status_string(obl_status s) {
     case OBL_ERR_CAPTURE:
       return "OBL_ERR_CAPTURE: the call needs more library scratch than its stream holds and the stream is "
              "capturing; make one call of this size on that stream before capturing";
+    case OBL_ERR_SCRATCH: return "OBL_ERR_SCRATCH: the call needs more scratch than the fixed array holds";
   }
   return "OBL_ERR_UNKNOWN";
 }
 
-// 0.3.0: per-stream scratch that is never freed, OBL_ERR_CAPTURE.
+// 0.3.0: per-stream scratch that is never freed, OBL_ERR_CAPTURE, the
+// allocation-free dbf_linear_noalloc.
 int obl_version(void) { return 300; }
 
 obl_status obl_pack_signs(const void* S, obl_dtype s_dtype, int64_t rows, int64_t K,
@@ -660,6 +703,15 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       float* workspace, void* Y, obl_dtype y_dtype, void* stream) {
   return dbf_impl(X, x_dtype, M, K, S2_packed, Kmid, S1_packed, N, b, m, a, scale_dtype, workspace, Y, y_dtype,
                   stream, SRC_POOL);
+}
+
+obl_status dbf_linear_noalloc(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                              const uint32_t* S2_packed, int64_t Kmid,
+                              const uint32_t* S1_packed, int64_t N,
+                              const void* b, const void* m, const void* a, obl_dtype scale_dtype,
+                              float* workspace, void* Y, obl_dtype y_dtype, void* stream) {
+  return dbf_impl(X, x_dtype, M, K, S2_packed, Kmid, S1_packed, N, b, m, a, scale_dtype, workspace, Y, y_dtype,
+                  stream, SRC_FIXED);
 }
 
 // Internal export for the test suite, not declared in obl.h: forces a path

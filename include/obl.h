@@ -78,7 +78,8 @@ typedef OBL_ENUM(obl_status_e) {
   OBL_ERR_HIP = 6,      /* the HIP runtime reported an error */
   OBL_ERR_INTERNAL = 7, /* unexpected internal failure */
   OBL_ERR_VALUE = 8,    /* a scalar argument is out of range (e.g. a negative epsilon) */
-  OBL_ERR_CAPTURE = 9   /* library scratch would have to grow while the call's stream is capturing */
+  OBL_ERR_CAPTURE = 9,  /* library scratch would have to grow while the call's stream is capturing */
+  OBL_ERR_SCRATCH = 10  /* dbf_linear_noalloc: the call needs more than its fixed scratch */
 } obl_status;
 
 typedef OBL_ENUM(obl_dtype_e) {
@@ -152,6 +153,30 @@ obl_status dbf_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
                       const uint32_t* S1_packed, int64_t N,
                       const void* b, const void* m, const void* a, obl_dtype scale_dtype,
                       float* workspace, void* Y, obl_dtype y_dtype, void* stream);
+
+/*
+ * dbf_linear_noalloc -- dbf_linear for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc): the same arguments, arithmetic and results, but its
+ *   scratch is a fixed 64 MiB device array (two 32 MiB slots: the copy of T1
+ *   plus the stages' own scratch in one, split-K partial sums in the other)
+ *   instead of the pool, and it calls no allocating routine.  Each GPU the
+ *   library runs on holds that array until the process ends.  Every call on
+ *   one GPU shares its array, and its contents persist from call to call
+ *   (nothing there needs to start at zero: every value is written before it
+ *   is read), so calls that overlap in time on one GPU -- on different
+ *   streams, host threads, or replays of captured graphs -- race and must be
+ *   serialised by the caller.  With bf16 X the limit is about
+ *   3 M Kmid <= 2^25 at decode sizes (M <= 8) and M Kmid <= 2^26 at prefill
+ *   sizes; a call that needs more returns OBL_ERR_SCRATCH before enqueuing
+ *   anything.
+ *   Errors: as dbf_linear, plus OBL_ERR_SCRATCH; never OBL_ERR_CAPTURE.
+ */
+obl_status dbf_linear_noalloc(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                              const uint32_t* S2_packed, int64_t Kmid,
+                              const uint32_t* S1_packed, int64_t N,
+                              const void* b, const void* m, const void* a, obl_dtype scale_dtype,
+                              float* workspace, void* Y, obl_dtype y_dtype, void* stream);
 
 /*
  * obl_svid -- Sign-Value-Independent Decomposition of a dense weight:

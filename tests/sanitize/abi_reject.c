@@ -49,6 +49,13 @@ int main(void) {
   expect("dbf alias", dbf_linear(X, OBL_BF16, 8, 4096, W, 3072, S1, 4096, B, G, A, OBL_F16, P(0x5000000000 + 64), Y,
                                  OBL_F32, NULL), OBL_ERR_ALIAS);
 
+  expect("dbf noalloc m0", dbf_linear_noalloc(NULL, OBL_BF16, 0, 4096, W, 3072, S1, 4096, B, G, A, OBL_F16, NULL,
+                                             NULL, OBL_F32, NULL), OBL_OK);
+  expect("dbf noalloc Kmid%32", dbf_linear_noalloc(X, OBL_BF16, 8, 4096, W, 3000, S1, 4096, B, G, A, OBL_F16, WS, Y,
+                                                  OBL_F32, NULL), OBL_ERR_SHAPE);
+  expect("dbf noalloc alias", dbf_linear_noalloc(X, OBL_BF16, 8, 4096, W, 3072, S1, 4096, B, G, A, OBL_F16,
+                                                P(0x5000000000 + 64), Y, OBL_F32, NULL), OBL_ERR_ALIAS);
+
   /* svid, transpose, backward */
   expect("svid iters", obl_svid(X, OBL_F16, 64, 64, 0, W, A, B, OBL_F16, NULL), OBL_ERR_SHAPE);
   expect("svid alias", obl_svid(X, OBL_F16, 64, 64, 4, W, P(0x2000000000 + 4), B, OBL_F16, NULL), OBL_ERR_ALIAS);

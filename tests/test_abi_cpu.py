@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in range(10):
+    for code in range(11):
         assert L.obl_status_string(code) != b"OBL_ERR_UNKNOWN"
     assert L.obl_status_string(99) == b"OBL_ERR_UNKNOWN"
     assert L.obl_version() >= 100
@@ -123,6 +123,23 @@ def test_dbf_m0_noop():
 ])
 def test_dbf_rejects(kw, code):
     assert dbf(**kw) == code
+
+
+def dbf_noalloc(X=X, M=8, K=4096, S2=W, Kmid=3072, S1_=S1, N=4096, bb=B_, m=A, a=P(0x80_0000_0000),
+                sd=b.OBL_F16, ws=WS, Y=Y, yd=b.OBL_F32, xd=b.OBL_BF16):
+    return L.dbf_linear_noalloc(X, xd, M, K, S2, Kmid, S1_, N, bb, m, a, sd, ws, Y, yd, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), b.OBL_OK),
+    (dict(S2=None), b.OBL_ERR_NULL),
+    (dict(Kmid=100), b.OBL_ERR_SHAPE),
+    (dict(sd=b.OBL_I8), b.OBL_ERR_DTYPE),
+    (dict(ws=P(0x60_0000_0002)), b.OBL_ERR_ALIGN),
+    (dict(ws=P(0x50_0000_0000)), b.OBL_ERR_ALIAS),
+])
+def test_dbf_noalloc_validates_like_dbf_linear(kw, code):
+    assert dbf_noalloc(**kw) == code == dbf(**kw)
 
 
 @pytest.mark.parametrize("args,code", [

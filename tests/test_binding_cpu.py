@@ -74,6 +74,11 @@ def test_dbf_rejects(kw):
     args.update(kw)
     with pytest.raises(ValueError):
         B.dbf_linear(**args)
+    if "workspace" in kw and "out" not in kw:
+        args["out"] = T(M, N, dt=torch.float32)
+    if "workspace" in args and "out" in args:
+        with pytest.raises(ValueError):
+            B.dbf_linear_noalloc(**args)
 
 
 def test_backward_rejects():
