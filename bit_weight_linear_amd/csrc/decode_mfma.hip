@@ -343,10 +343,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   // Slices in batches of 8 (clamped indexes, masked terms): every load of a
   // batch is in flight together, also for slice counts that are not a multiple
   // of 8 (a plain tail loop would wait once per slice).
-  // The slices' sums are added in slice order with compensated (Kahan)
-  // summation: the error stays that of one slice plus about two roundings
+  // The slices' sums in slice order: plainly up to 8 slices (K <= 4096, the
+  // whole-K kernel's cross-wave order), beyond that with compensated (Kahan)
+  // summation, so the error stays that of one slice plus a few roundings
   // however many slices K spans.
   float acc = 0.f, comp = 0.f;
+  const bool kahan = nslices > 8;   // uniform over the grid
   for (int s0 = 0; s0 < nslices; s0 += 8) {
     float v[8];
 #pragma unroll
@@ -354,10 +356,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (s0 + u < nslices) {   // uniform over the grid
-        const float y = v[u] - comp;
-        const float t = acc + y;
-        comp = (t - acc) - y;
-        acc = t;
+        if (kahan) {
+          const float y = v[u] - comp;
+          const float t = acc + y;
+          comp = (t - acc) - y;
+          acc = t;
+        } else {
+          acc += v[u];
+        }
       }
     }
   }
@@ -451,7 +457,7 @@ __device__ __forceinline__ void wk_wave_sync() {
 // backward (bf16 gin): gsum[n] = Σ_m gin[m][n] · y[m][n] over the block's
 // rows in order, and, with gout, gout[m][n] = y[m][n] · gscale[n] (fp32 or
 // bf16 as gout_bf16 says).
-template <int XM, typename ST, typename YT, int CPW, int PER, bool NT>
+template <int XM, typename ST, typename YT, int CPW, int PER, bool NT, bool MS>
 __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3,
@@ -554,16 +560,21 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
 #pragma unroll
         for (int a = 0; a < NA; ++a) acc[u][c][f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A wave's slices: the sum over one slice (terms of a set, then the sets in
-  // order) is added into a running total with compensated (Kahan) summation,
-  // so a lane's rounding error is that of one slice plus about two roundings
-  // however many slices it takes; with one slice per wave (K <= 4096) the
-  // total is that slice's sum exactly.
-  f32x4 ktot[CPW][RF], kcomp[CPW][RF];
+  // MS (K spans more slices than the workgroup has waves): a wave's slices
+  // are summed one slice at a time (terms of a set, then the sets in order)
+  // and each slice's sum is added into a running total with compensated
+  // (Kahan) summation, so a lane's rounding error is that of one slice plus
+  // about two roundings however long K is.  Without MS every wave has at most
+  // one slice and the fold below never runs (an instance of its own: the
+  // running total's registers and the fold measured 0.3 us slower at
+  // 16 x 4096 x 4096 even unused).
+  f32x4 ktot[MS ? CPW : 1][MS ? RF : 1], kcomp[MS ? CPW : 1][MS ? RF : 1];
+  if constexpr (MS) {
 #pragma unroll
-  for (int c = 0; c < CPW; ++c)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int f = 0; f < RF; ++f) ktot[c][f] = kcomp[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < RF; ++f) ktot[c][f] = kcomp[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   auto fold_slice = [&]() {
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -579,15 +590,19 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[u][c][f][a] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        const f32x4 y = sl - kcomp[c][f];
-        const f32x4 t = ktot[c][f] + y;
-        kcomp[c][f] = (t - ktot[c][f]) - y;
-        ktot[c][f] = t;
+        if constexpr (MS) {
+          const f32x4 y = sl - kcomp[c][f];
+          const f32x4 t = ktot[c][f] + y;
+          kcomp[c][f] = (t - ktot[c][f]) - y;
+          ktot[c][f] = t;
+        }
       }
   };
 
   for (int s = wave; s < nslices; s += WAVES) {
-    if (s != wave) fold_slice();   // uniform: the previous slice's sums into the total
+    if constexpr (MS) {
+      if (s != wave) fold_slice();   // uniform: the previous slice's sums into the total
+    }
     const int64_t step0 = (int64_t)s * DEC_STEPS;
     const int64_t k0 = step0 * 32;
     const int nsteps = (int)min((int64_t)DEC_STEPS, kw - step0);   // a multiple of 4
@@ -712,9 +727,30 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     wk_wave_sync();   // the next slice's DMAs overwrite this slice's LDS
   }
 
-  // The last slice (or zeros for a wave without one) into the total.
-  fold_slice();
-  const f32x4 (&tot)[CPW][RF] = ktot;
+  // Fixed summation order: terms of a set, then the sets in order; with MS,
+  // that sum of the last slice (or zeros) into the running total.
+  f32x4 tot[CPW][RF];
+  if constexpr (MS) {
+    fold_slice();
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) tot[c][f] = ktot[c][f];
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        tot[c][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < AU; ++u) {
+          f32x4 su = acc[u][c][f][0];
+#pragma unroll
+          for (int a = 1; a < NA; ++a) su = su + acc[u][c][f][a];
+          tot[c][f] = tot[c][f] + su;
+        }
+      }
+  }
   // Waves' sums through LDS: red[wave][row][column]; lane holds rows
   // 16f + 4g .. +3 of column 16c + j.  Added in wave order.
   __syncthreads();   // every wave is done with its staging region
@@ -732,20 +768,11 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
     const int o = tid + THREADS * r;
     const int m = o / NC, cl = o - (o / NC) * NC;
     if (o < 16 * RF * NC && m < M && n0 + cl < N) {
-      // The waves' totals in wave order, compensated (Kahan) as the slices
-      // within a wave, over the waves that had a slice: with at most one
-      // slice per wave this is the split kernel's slice reduction, term for
-      // term (a Kahan step that adds a zero would apply the compensation).
-      float v = 0.f, vc = 0.f;
+      // The waves' totals in wave order (at most 8 terms): with one slice
+      // per wave this is the split kernel's slice reduction, term for term.
+      float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        if (w < nslices) {   // uniform
-          const float y = red[(w * 16 * RF + m) * RS + cl] - vc;
-          const float t = v + y;
-          vc = (t - v) - y;
-          v = t;
-        }
-      }
+      for (int w = 0; w < WAVES; ++w) v += red[(w * 16 * RF + m) * RS + cl];
       const float y = v * post_o[r];
       const int64_t e = (int64_t)m * N + n0 + cl;
       Store<YT>::put(&Y[e], y);
@@ -774,14 +801,18 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
   }
 }
 
-template <int XM, typename ST, typename YT, int CPW, int PER, bool NT = true>
+template <int XM, typename ST, typename YT, int CPW, int PER, bool NT = true, bool MS = false>
 hipError_t launch_wk(const LinearArgs& a) {
   if constexpr (XM == WK_B2 && NT) {
     if (a.gsum) return launch_wk<XM, ST, YT, CPW, PER, false>(a);   // the backward's contractions
   }
+  if constexpr (!MS) {
+    // More slices than waves: the instance with the per-slice compensated fold.
+    if ((a.K / 32 + DEC_STEPS - 1) / DEC_STEPS > wk_waves(XM, PER, CPW)) return launch_wk<XM, ST, YT, CPW, PER, NT, true>(a);
+  }
   const int64_t blocks = (a.N + 16 * CPW - 1) / (16 * CPW);
   if (blocks > 0x7fffffff || a.M > 4 * PER) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_wk_kernel<XM, ST, YT, CPW, PER, NT>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((decode_wk_kernel<XM, ST, YT, CPW, PER, NT, MS>), dim3((unsigned)blocks),
                      dim3(64 * wk_waves(XM, PER, CPW)), wk_lds_bytes(XM, PER, CPW), a.stream,
                      static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N, static_cast<const f16_t*>(a.pre),
                      static_cast<const ST*>(a.post), static_cast<YT*>(a.Y), static_cast<bf16_t*>(a.T3),

@@ -12,7 +12,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "../../include/obl.h"
+#include "obl.h"
 #include "obl_internal.hpp"
 
 namespace obl {
