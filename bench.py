@@ -13,7 +13,16 @@ with fp16 scales, fp32 output.
 * roofline.achieved = algorithmic bytes of one launch (packed signs + X + a + b
   + Y) / average launch time over the timed region (HIP events on the stream
   the graph replays on).
-* cpu_baseline = the fp64 oracle on the same workload, timed on the host.
+* per_launch_distribution: median / p10 / p90 of the per-launch time over the
+  timed steps (an event between consecutive replays).
+* kernel_span: a second pass of the same arrangement whose launches record,
+  per workgroup, start and end in constant-clock ticks: the GEMV's own span
+  inside a launch (the rest of the per-launch time is the dispatch gap).
+* launch_floor_context: a read-only kernel over the same weight copies, the
+  runtime's copy of them and an empty kernel, launched the same way.
+* measured_peaks: the part's achievable streaming read and bf16 MFMA rate.
+* cpu_baseline = the fp64 oracle on the same workload, timed on the host, and
+  every workload's oracle call (dense-weight formation and product apart).
 * secondary = the other workloads (prefill GEMM TOPS, batched decode, DBF, the
   NEXT rows), timed the same way.
 * Before timing, every line's outputs are checked against a plain fp32 PyTorch
@@ -22,7 +31,7 @@ with fp16 scales, fp32 output.
   configuration has a full-size parity test there); here the oracle only runs
   in the cpu_baseline leg.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu-baseline] [--no-peaks]
 """
 from __future__ import annotations
 
@@ -98,19 +107,29 @@ class Timed:
         self.n = len(launches)
 
     def run(self, warmup: int, steps: int):
+        """Times `steps` replays with an event between consecutive replays (on the stream the replays
+        run on).  Returns the whole region's ms per step and per launch, and the median / p10 / p90 of
+        the per-launch time over the steps (each step's time / launches per step)."""
         torch = self.torch
         for _ in range(warmup):
             self.graph.replay()
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
+        for i in range(steps):
             self.graph.replay()
-        stop.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        ms = start.elapsed_time(stop)
-        return ms / steps, ms / (steps * self.n)   # ms per step, ms per launch
+        ms = evs[0].elapsed_time(evs[-1])
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) / self.n * 1e3 for i in range(steps))
+        q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+        return {"ms_step": ms / steps, "ms_launch": ms / (steps * self.n), "us_median": q(0.5),
+                "us_p10": q(0.1), "us_p90": q(0.9), "steps": steps}
+
+
+def dist(r):
+    """The per-launch distribution fields of a Timed.run result (us)."""
+    return {"us_median": round(r["us_median"], 4), "us_p10": round(r["us_p10"], 4), "us_p90": round(r["us_p90"], 4)}
 
 
 # ------------------------------------------------------------------ guards
@@ -158,6 +177,7 @@ def onebit_setup(torch, B, WL, i, rotate_bytes):
     err = t_err(torch, Y, Yref, S)
     del Spm1, Yref, S
     launches = [(lambda W=W, a=a, b=b: B.linear(X, W, a, b, out=Y)) for (W, a, b) in copies]
+    onebit_setup.last = {"X": X, "Y": Y, "copies": copies}   # the headline's span and floor passes reuse them
     return c, launches, err, R
 
 
@@ -228,35 +248,308 @@ def backward_setup(torch, B, WL, M, K, N, copies):
     return launches, err
 
 
-def cpu_baseline(WL, budget_s: float = 12.0):
-    """Time the fp64 oracle on workload 2 (the headline) for a bounded sample.
-    The only place bench.py uses the oracle."""
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def cpu_baseline(WL):
+    """The fp64 oracle timed on the host, the only place bench.py uses it.  The headline value is
+    the oracle's weight GB/s on the decode GEMV workload (whole calls); beside it every workload's
+    oracle call, with the dense-weight formation and the whole call timed separately (the product is
+    their difference), medians of a few calls (about 10-20 s of host work in all)."""
     import numpy as np
     import oracle as O
-    c = WL.workload(2)
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     except Exception:
         threads = 1
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 50):
-        t0 = time.perf_counter()
-        O.onebit_linear(c.X, c.W_sign, c.a, c.b)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
-    wbytes = c.N * c.K / 8
+
+    def timeit(f, n):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return _median(ts)
+
+    per = {}
+    for i in (1, 2, 3, 4, 5):
+        c = WL.workload(i)
+        n = 3 if i in (4, 5) else 7
+        if i == 5:
+            form = timeit(lambda: O.dbf_dense_weight(c.S1, c.S2, c.a, c.m, c.b), n)
+            full = timeit(lambda: O.dbf_linear(c.X, c.S1, c.S2, c.a, c.m, c.b), n)
+            M, K, N = c.X.shape[0], c.S2.shape[1], c.S1.shape[0]
+            wbytes = c.S2.shape[0] * (K + N) / 8
+        else:
+            form = timeit(lambda: O.onebit_dense_weight(c.W_sign, c.a, c.b), n)
+            full = timeit(lambda: O.onebit_linear(c.X, c.W_sign, c.a, c.b), n)
+            M, K, N = c.M, c.K, c.N
+            wbytes = N * K / 8
+        per[c.name] = {"calls": n, "ms_dense_weight": round(form * 1e3, 2), "ms_call": round(full * 1e3, 2),
+                       "ms_product": round((full - form) * 1e3, 2), "weight_GBps": round(wbytes / full / 1e9, 4),
+                       "GFLOPs_dense_eq": round(2.0 * M * N * K / full / 1e9, 2)}
+    head = per[WL.workload(2).name]
     try:
         affinity = len(os.sched_getaffinity(0))
     except AttributeError:
         affinity = None
-    return {"value": round(wbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} full calls of workload 1x4096x11008 (fp64 dense W = W_sign*(a b^T) "
-                      f"then X W^T), median {t * 1e3:.1f} ms per call; weight bytes N*K/8 per call; "
-                      f"dense-W formation is single-threaded NumPy, the product uses {threads} BLAS threads; "
-                      f"host os.cpu_count() = {os.cpu_count()}, affinity {affinity}, "
-                      f"OPENBLAS_NUM_THREADS = {os.environ.get('OPENBLAS_NUM_THREADS')}"}
+    return {"value": head["weight_GBps"], "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{head['calls']} whole calls of the 1x4096x11008 decode GEMV (fp64 dense W = W_sign*(a b^T), "
+                      f"then X W^T), median {head['ms_call']} ms per call, weight bytes N*K/8 per call; every "
+                      f"workload's oracle call in per_config; dense-W formation is single-threaded NumPy, the "
+                      f"products use {threads} BLAS threads; host os.cpu_count() = {os.cpu_count()}, "
+                      f"affinity {affinity}, OPENBLAS_NUM_THREADS = {os.environ.get('OPENBLAS_NUM_THREADS')}",
+            "per_config": per}
+
+
+def kernel_span(torch, B, X, copies, N, Y, R):
+    """Per-launch kernel span of the decode GEMV in the timed arrangement: every workgroup records its
+    start and end (constant-clock ticks) and a launch's span is the last end minus the first start.
+    Ticks are converted with the device's wall-clock rate (HIP attribute); the rate implied by events
+    around the same replay is reported beside it as a check."""
+    span = torch.full((R, 2 * N), -1, dtype=torch.int64, device="cuda")
+    t = Timed(torch, [(lambda r=r, W=W, a=a, b=b: B.linear_span(X, W, a, b, Y, span[r]))
+                      for r, (W, a, b) in enumerate(copies)])
+    t.run(3, 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    span.fill_(-1)
+    torch.cuda.synchronize()
+    e0.record()
+    t.graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    sp = span.view(R, -1, 2).cpu()
+    starts, ends = [], []
+    for r in range(R):
+        v = sp[r][sp[r][:, 0] >= 0]
+        starts.append(int(v[:, 0].min()))
+        ends.append(int(v[:, 1].max()))
+    ticks_per_us_events = (ends[-1] - starts[0]) / (ms * 1e3)   # first start to last end ~ the replay
+    khz = B.lib.obl_internal_wallclock_khz()
+    ticks_per_us = khz / 1e3 if khz > 0 else ticks_per_us_events
+    spans = sorted((e - s_) / ticks_per_us for s_, e in zip(starts, ends))
+    q = lambda f: spans[min(len(spans) - 1, int(round(f * (len(spans) - 1))))]
+    out = {"us_mean": round(sum(spans) / len(spans), 4), "us_median": round(q(0.5), 4),
+           "us_p10": round(q(0.1), 4), "us_p90": round(q(0.9), 4),
+           "clock_MHz": round(ticks_per_us, 3), "clock_MHz_from_events": round(ticks_per_us_events, 3),
+           "launches": R,
+           "instrumented_us_per_launch": round(ms * 1e3 / R, 4)}
+    del t, span
+    return out
+
+
+def measured_peaks(torch, B):
+    """The part's achievable streaming-read bandwidth (2 GiB read once per launch) and bf16 matrix-core
+    rate (an MFMA loop on pseudo-random operands), as context for the published peaks."""
+    buf = torch.zeros(1 << 31, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        B.peak_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        B.peak_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    fsink = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
+    B.peak_mfma(2000, fsink)
+    torch.cuda.synchronize()
+    e0.record()
+    flops = 0.0
+    for _ in range(3):
+        flops += B.peak_mfma(20000, fsink)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"hbm_read_GBps": round(read_gbs, 1), "hbm_read_frac_of_spec": round(read_gbs / HBM_PEAK_GBS, 4),
+            "bf16_mfma_TFLOPs": round(tflops, 1), "bf16_mfma_frac_of_spec": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "what": "streaming read of 2 GiB (16-byte non-temporal loads, 8 workgroups of 256 per CU); "
+                    "a loop of independent 32x32x16 bf16 MFMAs, two waves per SIMD, pseudo-random bf16 operands"}
+
+
+PAGE_CONTEXT = ("DBF page, 'Resultaten / Snelheid': DBF runs matrix-vector products 2x-3.5x faster than the FP16 "
+                "dense layer (depending on the compression ratio) and token generation 2.0x-2.9x faster, on an "
+                "NVIDIA RTX 4090 -- another machine and a relative figure, context only")
+
+
+def line_gemm(torch, B, WL, args, rot, sec, R, wbytes):
+    """Workload 4: prefill GEMM, M = 2048."""
+    import numpy as np
+    c4, l4, e4, R4 = onebit_setup(torch, B, WL, 4, min(rot, 64 << 20))
+    assert e4 <= 1e-2, "workload 4 disagrees with the fp32 guard"
+    t4 = Timed(torch, l4)
+    r4 = t4.run(2, max(3, args.steps // 4))
+    flops = 2.0 * c4.M * c4.N * c4.K
+    tflops = flops / (r4["ms_launch"] * 1e-3) / 1e12
+    sec[c4.name] = {"us_per_launch": round(r4["ms_launch"] * 1e3, 2), **dist(r4), "TOPS": round(tflops, 2),
+                    "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
+                    "check_vs_torch_fp32": float(f"{e4:.3e}"), "copies": R4}
+    log(f"[bench] {c4.name}: {r4['ms_launch'] * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    del l4, t4
+    onebit_setup.last = None
+    torch.cuda.empty_cache()
+
+
+def line_decode(torch, B, WL, args, rot, sec, R, wbytes):
+    """Workloads 3, 1: decode kernel."""
+    import numpy as np
+    for i in (3, 1):
+        ci, li, ei, Ri = onebit_setup(torch, B, WL, i, rot if i == 3 else (64 << 20))
+        assert ei <= 1e-4, f"workload {i} disagrees with the fp32 guard"
+        ti = Timed(torch, li)
+        ri = ti.run(args.warmup, args.steps)
+        msi = ri["ms_launch"]
+        wb = ci.N * ci.K / 8
+        ab = (wb + ci.M * ci.K * (4 if ci.x_dtype == "f32" else 2)
+              + (ci.N + ci.K) * (4 if ci.scale_dtype == "f32" else 2) + ci.M * ci.N * 4)
+        sec[ci.name] = {"us_per_launch": round(msi * 1e3, 3), **dist(ri),
+                        "weight_GBps": round(wb / (msi * 1e-3) / 1e9, 1),
+                        "algorithmic_bytes": int(ab), "ideal_us_hbm": round(ab / HBM_PEAK_GBS / 1e3, 4),
+                        "hbm_frac": round(ab / (msi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "bound": "latency (launch and one HBM round trip; the HBM time is a fraction of it)",
+                        "check_vs_torch_fp32": float(f"{ei:.3e}"), "copies": Ri}
+        log(f"[bench] {ci.name}: {msi * 1e3:.2f} us")
+        del li, ti
+        onebit_setup.last = None
+
+def line_dbf(torch, B, WL, args, rot, sec, R, wbytes):
+    """Workload 5: DBF."""
+    import numpy as np
+    c5, l5, e5, R5 = dbf_setup(torch, B, WL, rot)
+    assert e5 <= 1e-4, "workload 5 disagrees with the fp32 guard"
+    t5 = Timed(torch, l5)
+    r5 = t5.run(args.warmup, args.steps)
+    ms5 = r5["ms_launch"]
+    wb5 = c5.Kmid * (c5.K + c5.N) / 8
+    ab5 = wb5 + c5.M * c5.K * 2 + (c5.K + c5.Kmid + c5.N) * 2 + 2 * c5.M * c5.Kmid * 4 + c5.M * c5.N * 4
+    sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), **dist(r5),
+                    "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
+                    "algorithmic_bytes": int(ab5), "ideal_us_hbm": round(ab5 / HBM_PEAK_GBS / 1e3, 4),
+                    "hbm_frac": round(ab5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "bound": "latency (two stages, one launch each: stage 2 reads the exact bf16 terms of T1)",
+                    "check_vs_torch_fp32": float(f"{e5:.3e}"), "copies": R5,
+                    "stages_per_call": 2, "context": PAGE_CONTEXT}
+    log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
+    del l5, t5
+
+def line_dbfpre(torch, B, WL, args, rot, sec, R, wbytes):
+    """DBF prefill (M = 512, Kmid = 3072: 1.5 sign bits per weight)."""
+    import numpy as np
+    c6, l6, e6, R6 = dbf_prefill_setup(torch, B, WL)
+    assert e6 <= 1.5e-2, "the DBF prefill disagrees with the fp32 guard"
+    t6 = Timed(torch, l6)
+    r6 = t6.run(2, max(3, args.steps // 4))
+    ms6 = r6["ms_launch"]
+    fl6 = 2.0 * c6.X.shape[0] * c6.S2.shape[0] * (c6.S2.shape[1] + c6.S1.shape[0])
+    tf6 = fl6 / (ms6 * 1e-3) / 1e12
+    sec[c6.name] = {"us_per_call": round(ms6 * 1e3, 2), **dist(r6), "TOPS": round(tf6, 2),
+                    "mfma_frac": round(tf6 / BF16_PEAK_TFLOPS, 4),
+                    "check_vs_torch_fp32": float(f"{e6:.3e}"), "copies": R6}
+    log(f"[bench] {c6.name}: {ms6 * 1e3:.1f} us per call, {tf6:.1f} TFLOP/s")
+    del l6, t6
+
+def line_bwd(torch, B, WL, args, rot, sec, R, wbytes):
+    """Backward of the layer at the batched-decode shape."""
+    import numpy as np
+    l7, e7 = backward_setup(torch, B, WL, 16, 4096, 4096, copies=64)
+    assert e7 <= 1e-4, "the backward disagrees with the fp32 guard"
+    t7 = Timed(torch, l7)
+    r7 = t7.run(args.warmup, args.steps)
+    ms7 = r7["ms_launch"]
+    sec["backward-16x4096x4096"] = {"us_per_call": round(ms7 * 1e3, 3), **dist(r7),
+                                    "weight_GBps": round(2 * 4096 * 4096 / 8 / (ms7 * 1e-3) / 1e9, 1),
+                                    "check_vs_torch_fp32": float(f"{e7:.3e}"), "copies": 64,
+                                    "note": "weight bytes counted twice: W and its transposed packing"}
+    log(f"[bench] backward-16x4096x4096: {ms7 * 1e3:.2f} us per call")
+    del l7, t7
+
+def line_svid(torch, B, WL, args, rot, sec, R, wbytes):
+    """SVID conversion of the headline layer's dense fp16 weight (32 power iterations)."""
+    import numpy as np
+    rng8 = np.random.default_rng(8)
+    Wd = torch.from_numpy(WL.round_to(rng8.standard_normal((11008, 4096)) * 0.02, "f16")).to(torch.float16).cuda()
+    P8, a8, b8 = B.svid(Wd, iters=32)
+    assert bool(torch.isfinite(a8.float()).all() and (a8.float() > 0).all() and (b8.float() > 0).all()), \
+        "SVID scales not finite and positive"
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for k in range(3):
+        B.svid(Wd, iters=32)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    per8 = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(3))
+    ms8 = ev[0].elapsed_time(ev[3]) / 3
+    passes = 32 + 2                          # |W| reads: one per (fused) iteration, the final row pass, Sign(W)
+    sec["svid-11008x4096-f16-32iters"] = {"ms_per_conversion": round(ms8, 3),
+                                          "ms_min": round(per8[0], 3), "ms_max": round(per8[-1], 3),
+                                          "weight_read_GBps": round(passes * Wd.numel() * 2 / (ms8 * 1e-3) / 1e9, 1)}
+    log(f"[bench] svid-11008x4096-f16-32iters: {ms8:.3f} ms per conversion")
+    del Wd, P8, a8, b8
+
+def line_ln(torch, B, WL, args, rot, sec, R, wbytes):
+    """LayerNorm after the layer: the row kernel alone at the prefill output shape."""
+    import numpy as np
+    M9, N9 = 2048, 14336
+    rng9 = np.random.default_rng(9)
+    Y9 = [torch.from_numpy(rng9.standard_normal((M9, N9)) * 2 + 1).to(torch.float32).cuda() for _ in range(4)]
+    g9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.5 + 1, "f16")).to(torch.float16).cuda()
+    be9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.1, "f16")).to(torch.float16).cuda()
+    Z9 = torch.empty((M9, N9), dtype=torch.bfloat16, device="cuda")
+    B.layernorm(Y9[0], 1e-5, g9, be9, out=Z9)
+    z9ref = torch.nn.functional.layer_norm(Y9[0], (N9,), g9.float(), be9.float(), 1e-5)
+    e9 = float(((Z9.float() - z9ref).abs() / (z9ref.abs() + 1.0)).max())
+    del z9ref
+    assert e9 <= 2.0 ** -7, "the LayerNorm disagrees with the fp32 guard"
+    t9 = Timed(torch, [(lambda y=y: B.layernorm(y, 1e-5, g9, be9, out=Z9)) for y in Y9])
+    r9 = t9.run(args.warmup, args.steps)
+    ms9 = r9["ms_launch"]
+    by9 = M9 * N9 * (4 + 2) + 2 * N9 * 2
+    sec["layernorm-2048x14336-f32-bf16"] = {
+        "us_per_launch": round(ms9 * 1e3, 3), **dist(r9), "GBps": round(by9 / (ms9 * 1e-3) / 1e9, 1),
+        "hbm_frac": round(by9 / (ms9 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
+        "algorithmic_bytes": by9, "check_vs_torch_fp32": float(f"{e9:.3e}")}
+    log(f"[bench] layernorm-2048x14336: {ms9 * 1e3:.2f} us, {by9 / (ms9 * 1e-3) / 1e9:.0f} GB/s")
+    del t9, Y9, Z9
+
+def line_lnlin(torch, B, WL, args, rot, sec, R, wbytes):
+    """The decode layer followed by LayerNorm in one call (headline shape)."""
+    import numpy as np
+    c10 = WL.workload(2)
+    X10 = torch.from_numpy(c10.X).to(torch.float32).to(torch.bfloat16).cuda()
+    S10 = torch.from_numpy(c10.W_sign).cuda()
+    W10 = B.pack_signs(S10)
+    a10 = torch.from_numpy(c10.a).to(torch.float32).to(torch.float16).cuda()
+    b10 = torch.from_numpy(c10.b).to(torch.float32).to(torch.float16).cuda()
+    reps10 = [(W10, a10, b10)] + [(W10.clone(), a10.clone(), b10.clone()) for _ in range(R - 1)]
+    ws10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
+    Z10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
+    B.linear_layernorm(X10, W10, a10, b10, 1e-5, workspace=ws10, out=Z10)
+    y10, _ = t_linear(torch, X10, S10, a10, b10)
+    e10 = float((Z10 - torch.nn.functional.layer_norm(y10, (c10.N,), None, None, 1e-5)).abs().max())
+    del S10, y10
+    assert e10 <= 1e-3, "the layer + LayerNorm disagrees with the fp32 guard"
+    t10 = Timed(torch, [(lambda w=w, a=a, b=b: B.linear_layernorm(X10, w, a, b, 1e-5, workspace=ws10, out=Z10))
+                        for (w, a, b) in reps10])
+    r10 = t10.run(args.warmup, args.steps)
+    ms10 = r10["ms_launch"]
+    sec[f"linear-layernorm-{c10.name}"] = {"us_per_call": round(ms10 * 1e3, 3), **dist(r10),
+                                           "weight_GBps": round(wbytes / (ms10 * 1e-3) / 1e9, 1),
+                                           "check_vs_torch_fp32_abs": float(f"{e10:.3e}"), "copies": R,
+                                           "launches_per_call": 2}
+    log(f"[bench] linear-layernorm-{c10.name}: {ms10 * 1e3:.2f} us per call")
+    del t10, reps10
+    torch.cuda.empty_cache()
+
+
+LINES = {"gemm": line_gemm, "decode": line_decode, "dbf": line_dbf, "dbfpre": line_dbfpre, "bwd": line_bwd,
+         "svid": line_svid, "ln": line_ln, "lnlin": line_lnlin}
 
 
 def main():
@@ -267,6 +560,9 @@ def main():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--only", choices=["gemv"] + list(LINES), default=None,
+                    help="profiling runs: time one line alone and print it (not the benchmark's contract line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware-counter runs)")
@@ -284,14 +580,23 @@ def main():
     B = load_binding()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rot = int(args.rotate_gib * (1 << 30))
+    torch.backends.cuda.matmul.allow_tf32 = False    # the guards compare against plain fp32 products
+    if args.only not in (None, "gemv"):
+        c2 = WL.workload(2)
+        sec = {}
+        LINES[args.only](torch, B, WL, args, rot, sec, 190, c2.N * c2.K // 8)
+        print(json.dumps({"only": args.only, "secondary": sec}), flush=True)
+        return
+    if args.only == "gemv":
+        args.no_secondary = args.no_peaks = args.no_cpu_baseline = True
 
     # ---------------- headline: workload 2, M = 1 decode GEMV
-    torch.backends.cuda.matmul.allow_tf32 = False    # the guards compare against plain fp32 products
     c, launches, err, R = onebit_setup(torch, B, WL, 2, rot)
     log(f"[bench] {c.name}: guard vs fp32 torch, max normalised error {err:.3e}; {R} weight copies")
     assert err <= 1e-4, "the timed configuration disagrees with the fp32 guard"
     t = Timed(torch, launches)
-    ms_step, ms_launch = t.run(args.warmup, args.steps)
+    r = t.run(args.warmup, args.steps)
+    ms_step, ms_launch = r["ms_step"], r["ms_launch"]
     wbytes = c.N * c.K // 8
     alg_bytes = wbytes + c.M * c.K * 2 + c.N * 2 + c.K * 2 + c.M * c.N * 4
     value = wbytes * R / (ms_step * 1e-3) / 1e9
@@ -318,179 +623,72 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "us_per_launch": round(ms_launch * 1e3, 4),
+        "per_launch_distribution": dist(r),
         "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
         "check_vs_torch_fp32": float(f"{err:.3e}"),
         "parity": "against the fp64 oracle in tests/test_gpu_parity.py (test_workload2_decode_gemv, full size)",
+        "context_pages": PAGE_CONTEXT,
     }
-    del launches, t
-    torch.cuda.empty_cache()
-    # Context for the headline: the runtime's own device-to-device copy of the same weight bytes,
-    # launched the same way (R distinct sources, one graph replay).  A copy streams the bytes once
-    # and writes as many, with no arithmetic: its per-launch time is a practical floor for a
-    # kernel that must read these weights from HBM once per launch.
-    srcs = [torch.ones(wbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    # The GEMV's own span inside each launch (first workgroup start to last workgroup end), measured
+    # in a second pass of the same arrangement whose launches record it: the dispatch gap between
+    # back-to-back kernels is the rest of the per-launch time.
+    hx = onebit_setup.last
+    copies = hx["copies"]
+    del t
+    sp = kernel_span(torch, B, hx["X"], copies, c.N, hx["Y"], R)
+    sp["frac_over_span"] = round(alg_bytes / (sp["us_mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    out["kernel_span"] = sp
+    log(f"[bench] GEMV span inside a launch {sp['us_mean']:.3f} us (clock {sp['clock_MHz']} MHz), "
+        f"per launch {ms_launch * 1e3:.3f} us")
+    # Context for the headline, launched the same way (R distinct sources, one graph replay): a plain
+    # read of the same weight bytes (the same copies), the runtime's device-to-device copy, and an
+    # empty kernel.  No kernel launched this way takes less than the empty one; the read is the
+    # practical floor of a kernel that must read these weights once per launch.
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    tr = Timed(torch, [(lambda W=W: B.peak_read(W, sink)) for (W, _, _) in copies])
+    ms_read = tr.run(args.warmup, args.steps)["ms_launch"]
+    del tr
+    floor = {"read_us_per_launch": round(ms_read * 1e3, 4),
+             "read_what": f"read-only kernel over the same {wbytes} weight bytes (16-byte non-temporal loads, "
+                          f"nothing written), {R} distinct copies in one graph replay",
+             "gemv_over_read": round(ms_launch / ms_read, 3)}
+    srcs = [W.view(torch.uint8).reshape(-1) for (W, _, _) in copies]
     dst = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
     tc = Timed(torch, [(lambda s_=s_: dst.copy_(s_)) for s_ in srcs])
-    _, ms_copy = tc.run(args.warmup, args.steps)
-    out["launch_floor_context"] = {
-        "what": f"device-to-device copy of {wbytes} bytes per launch (torch copy_), {R} distinct sources "
-                f"in one graph replay, same arrangement as the timed GEMV launches",
-        "us_per_launch": round(ms_copy * 1e3, 4),
-        "read_GBps": round(wbytes / (ms_copy * 1e-3) / 1e9, 1),
-        "gemv_over_copy": round(ms_launch / ms_copy, 3)}
-    log(f"[bench] context: copy of the weight bytes {ms_copy * 1e3:.2f} us per launch "
-        f"(GEMV {ms_launch * 1e3:.2f} us)")
+    ms_copy = tc.run(args.warmup, args.steps)["ms_launch"]
+    floor["copy_us_per_launch"] = round(ms_copy * 1e3, 4)
+    floor["gemv_over_copy"] = round(ms_launch / ms_copy, 3)
     del srcs, dst, tc
-    torch.cuda.empty_cache()
-    # The fixed cost of a launch in the same arrangement: a kernel that spins for zero cycles
-    # (torch's own test helper), R of them in one graph replay.  No kernel launched this way
-    # takes less; what the GEMV and the copy add on top of it is their memory and arithmetic.
     try:
         te = Timed(torch, [(lambda: torch.cuda._sleep(0)) for _ in range(R)])
-        _, ms_empty = te.run(args.warmup, args.steps)
-        out["launch_floor_context"]["empty_kernel_us_per_launch"] = round(ms_empty * 1e3, 4)
-        out["launch_floor_context"]["gemv_above_empty_us"] = round((ms_launch - ms_empty) * 1e3, 4)
-        log(f"[bench] context: empty kernel {ms_empty * 1e3:.2f} us per launch")
+        ms_empty = te.run(args.warmup, args.steps)["ms_launch"]
+        floor["empty_kernel_us_per_launch"] = round(ms_empty * 1e3, 4)
+        floor["gemv_above_empty_us"] = round((ms_launch - ms_empty) * 1e3, 4)
+        floor["read_above_empty_us"] = round((ms_read - ms_empty) * 1e3, 4)
         del te
     except (AttributeError, RuntimeError) as e:   # helper missing on this build
         log(f"[bench] context: no empty-kernel timing ({e})")
+    out["launch_floor_context"] = floor
+    log(f"[bench] context: read of the weights {ms_read * 1e3:.2f} us, copy {ms_copy * 1e3:.2f} us, "
+        f"empty kernel {floor.get('empty_kernel_us_per_launch')} us per launch (GEMV {ms_launch * 1e3:.2f} us)")
+    del launches, copies, hx
+    onebit_setup.last = None
+    torch.cuda.empty_cache()
 
     # ---------------- secondary workloads
     if not args.no_secondary:
         sec = {}
-        # workload 4: prefill GEMM, M = 2048
-        c4, l4, e4, R4 = onebit_setup(torch, B, WL, 4, min(rot, 64 << 20))
-        assert e4 <= 1e-2, "workload 4 disagrees with the fp32 guard"
-        t4 = Timed(torch, l4)
-        ms4_step, ms4 = t4.run(2, max(3, args.steps // 4))
-        flops = 2.0 * c4.M * c4.N * c4.K
-        tflops = flops / (ms4 * 1e-3) / 1e12
-        sec[c4.name] = {"us_per_launch": round(ms4 * 1e3, 2), "TOPS": round(tflops, 2),
-                        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
-                        "check_vs_torch_fp32": float(f"{e4:.3e}"), "copies": R4}
-        log(f"[bench] {c4.name}: {ms4 * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
-        del l4, t4
-        torch.cuda.empty_cache()
-        # workloads 1, 3: decode kernel
-        for i in (3, 1):
-            ci, li, ei, Ri = onebit_setup(torch, B, WL, i, rot if i == 3 else (64 << 20))
-            assert ei <= 1e-4, f"workload {i} disagrees with the fp32 guard"
-            ti = Timed(torch, li)
-            _, msi = ti.run(args.warmup, args.steps)
-            wb = ci.N * ci.K / 8
-            ab = (wb + ci.M * ci.K * (4 if ci.x_dtype == "f32" else 2)
-                  + (ci.N + ci.K) * (4 if ci.scale_dtype == "f32" else 2) + ci.M * ci.N * 4)
-            sec[ci.name] = {"us_per_launch": round(msi * 1e3, 3),
-                            "weight_GBps": round(wb / (msi * 1e-3) / 1e9, 1),
-                            "algorithmic_bytes": int(ab), "ideal_us_hbm": round(ab / HBM_PEAK_GBS / 1e3, 4),
-                            "hbm_frac": round(ab / (msi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "bound": "latency (launch and one HBM round trip; the HBM time is a fraction of it)",
-                            "check_vs_torch_fp32": float(f"{ei:.3e}"), "copies": Ri}
-            log(f"[bench] {ci.name}: {msi * 1e3:.2f} us")
-            del li, ti
-        # workload 5: DBF
-        c5, l5, e5, R5 = dbf_setup(torch, B, WL, rot)
-        assert e5 <= 1e-4, "workload 5 disagrees with the fp32 guard"
-        t5 = Timed(torch, l5)
-        _, ms5 = t5.run(args.warmup, args.steps)
-        wb5 = c5.Kmid * (c5.K + c5.N) / 8
-        ab5 = wb5 + c5.M * c5.K * 2 + (c5.K + c5.Kmid + c5.N) * 2 + 2 * c5.M * c5.Kmid * 4 + c5.M * c5.N * 4
-        sec[c5.name] = {"us_per_call": round(ms5 * 1e3, 3), "weight_GBps": round(wb5 / (ms5 * 1e-3) / 1e9, 1),
-                        "algorithmic_bytes": int(ab5), "ideal_us_hbm": round(ab5 / HBM_PEAK_GBS / 1e3, 4),
-                        "hbm_frac": round(ab5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "bound": "latency (two stages, one launch each: stage 2 reads the exact bf16 terms of T1)",
-                        "check_vs_torch_fp32": float(f"{e5:.3e}"), "copies": R5,
-                        "stages_per_call": 2}
-        log(f"[bench] {c5.name}: {ms5 * 1e3:.2f} us per call")
-        del l5, t5
-        # DBF prefill (M = 512, Kmid = 3072: 1.5 sign bits per weight)
-        c6, l6, e6, R6 = dbf_prefill_setup(torch, B, WL)
-        assert e6 <= 1.5e-2, "the DBF prefill disagrees with the fp32 guard"
-        t6 = Timed(torch, l6)
-        _, ms6 = t6.run(2, max(3, args.steps // 4))
-        fl6 = 2.0 * c6.X.shape[0] * c6.S2.shape[0] * (c6.S2.shape[1] + c6.S1.shape[0])
-        tf6 = fl6 / (ms6 * 1e-3) / 1e12
-        sec[c6.name] = {"us_per_call": round(ms6 * 1e3, 2), "TOPS": round(tf6, 2),
-                        "mfma_frac": round(tf6 / BF16_PEAK_TFLOPS, 4),
-                        "check_vs_torch_fp32": float(f"{e6:.3e}"), "copies": R6}
-        log(f"[bench] {c6.name}: {ms6 * 1e3:.1f} us per call, {tf6:.1f} TFLOP/s")
-        del l6, t6
-        # backward of the layer at the batched-decode shape (two sign contractions + the grads kernel)
-        l7, e7 = backward_setup(torch, B, WL, 16, 4096, 4096, copies=64)
-        assert e7 <= 1e-4, "the backward disagrees with the fp32 guard"
-        t7 = Timed(torch, l7)
-        _, ms7 = t7.run(args.warmup, args.steps)
-        sec["backward-16x4096x4096"] = {"us_per_call": round(ms7 * 1e3, 3),
-                                        "weight_GBps": round(2 * 4096 * 4096 / 8 / (ms7 * 1e-3) / 1e9, 1),
-                                        "check_vs_torch_fp32": float(f"{e7:.3e}"), "copies": 64,
-                                        "note": "weight bytes counted twice: W and its transposed packing"}
-        log(f"[bench] backward-16x4096x4096: {ms7 * 1e3:.2f} us per call")
-        del l7, t7
-        # SVID conversion of the headline layer's dense fp16 weight (32 power iterations)
-        rng8 = np.random.default_rng(8)
-        Wd = torch.from_numpy(WL.round_to(rng8.standard_normal((11008, 4096)) * 0.02, "f16")).to(torch.float16).cuda()
-        P8, a8, b8 = B.svid(Wd, iters=32)
-        assert bool(torch.isfinite(a8.float()).all() and (a8.float() > 0).all() and (b8.float() > 0).all()), \
-            "SVID scales not finite and positive"
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(3):
-            B.svid(Wd, iters=32)
-        ev1.record()
-        torch.cuda.synchronize()
-        ms8 = ev0.elapsed_time(ev1) / 3
-        passes = 32 + 2                          # |W| reads: one per (fused) iteration, the final row pass, Sign(W)
-        sec["svid-11008x4096-f16-32iters"] = {"ms_per_conversion": round(ms8, 3),
-                                              "weight_read_GBps": round(passes * Wd.numel() * 2 / (ms8 * 1e-3) / 1e9, 1)}
-        log(f"[bench] svid-11008x4096-f16-32iters: {ms8:.3f} ms per conversion")
-        del Wd, P8, a8, b8
-        # LayerNorm after the layer: the row kernel alone at the prefill output shape
-        # (fp32 Y -> bf16 Z, fp16 gamma/beta), over 4 copies of Y so no replay hits in cache
-        M9, N9 = 2048, 14336
-        rng9 = np.random.default_rng(9)
-        Y9 = [torch.from_numpy(rng9.standard_normal((M9, N9)) * 2 + 1).to(torch.float32).cuda() for _ in range(4)]
-        g9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.5 + 1, "f16")).to(torch.float16).cuda()
-        be9 = torch.from_numpy(WL.round_to(rng9.standard_normal(N9) * 0.1, "f16")).to(torch.float16).cuda()
-        Z9 = torch.empty((M9, N9), dtype=torch.bfloat16, device="cuda")
-        B.layernorm(Y9[0], 1e-5, g9, be9, out=Z9)
-        z9ref = torch.nn.functional.layer_norm(Y9[0], (N9,), g9.float(), be9.float(), 1e-5)
-        e9 = float(((Z9.float() - z9ref).abs() / (z9ref.abs() + 1.0)).max())
-        del z9ref
-        assert e9 <= 2.0 ** -7, "the LayerNorm disagrees with the fp32 guard"
-        t9 = Timed(torch, [(lambda y=y: B.layernorm(y, 1e-5, g9, be9, out=Z9)) for y in Y9])
-        _, ms9 = t9.run(args.warmup, args.steps)
-        by9 = M9 * N9 * (4 + 2) + 2 * N9 * 2
-        sec["layernorm-2048x14336-f32-bf16"] = {
-            "us_per_launch": round(ms9 * 1e3, 3), "GBps": round(by9 / (ms9 * 1e-3) / 1e9, 1),
-            "hbm_frac": round(by9 / (ms9 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
-            "algorithmic_bytes": by9, "check_vs_torch_fp32": float(f"{e9:.3e}")}
-        log(f"[bench] layernorm-2048x14336: {ms9 * 1e3:.2f} us, {by9 / (ms9 * 1e-3) / 1e9:.0f} GB/s")
-        del t9, Y9, Z9
-        # the decode layer followed by LayerNorm in one call (headline shape)
-        c10 = WL.workload(2)
-        X10 = torch.from_numpy(c10.X).to(torch.float32).to(torch.bfloat16).cuda()
-        S10 = torch.from_numpy(c10.W_sign).cuda()
-        W10 = B.pack_signs(S10)
-        a10 = torch.from_numpy(c10.a).to(torch.float32).to(torch.float16).cuda()
-        b10 = torch.from_numpy(c10.b).to(torch.float32).to(torch.float16).cuda()
-        reps10 = [(W10, a10, b10)] + [(W10.clone(), a10.clone(), b10.clone()) for _ in range(R - 1)]
-        ws10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
-        Z10 = torch.empty((1, c10.N), dtype=torch.float32, device="cuda")
-        B.linear_layernorm(X10, W10, a10, b10, 1e-5, workspace=ws10, out=Z10)
-        y10, _ = t_linear(torch, X10, S10, a10, b10)
-        e10 = float((Z10 - torch.nn.functional.layer_norm(y10, (c10.N,), None, None, 1e-5)).abs().max())
-        del S10, y10
-        assert e10 <= 1e-3, "the layer + LayerNorm disagrees with the fp32 guard"
-        t10 = Timed(torch, [(lambda w=w, a=a, b=b: B.linear_layernorm(X10, w, a, b, 1e-5, workspace=ws10, out=Z10))
-                            for (w, a, b) in reps10])
-        _, ms10 = t10.run(args.warmup, args.steps)
-        sec[f"linear-layernorm-{c10.name}"] = {"us_per_call": round(ms10 * 1e3, 3),
-                                               "weight_GBps": round(wbytes / (ms10 * 1e-3) / 1e9, 1),
-                                               "check_vs_torch_fp32_abs": float(f"{e10:.3e}"), "copies": R,
-                                               "launches_per_call": 2}
-        log(f"[bench] linear-layernorm-{c10.name}: {ms10 * 1e3:.2f} us per call")
-        del t10, reps10
+        for key, fn in LINES.items():
+            if args.only in (None, key):
+                fn(torch, B, WL, args, rot, sec, R, wbytes)
+                onebit_setup.last = None
+                torch.cuda.empty_cache()
         out["secondary"] = sec
+
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks(torch, B)
+        log(f"[bench] measured peaks: {out['measured_peaks']['hbm_read_GBps']} GB/s read, "
+            f"{out['measured_peaks']['bf16_mfma_TFLOPs']} TFLOP/s bf16 MFMA")
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20

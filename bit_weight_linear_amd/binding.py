@@ -64,6 +64,16 @@ lib.obl_version.restype = _int
 # kernel for the calling thread; see forced_kernels below.
 lib.obl_internal_force_kernels.argtypes = [_int, _int, _int]
 lib.obl_internal_force_kernels.restype = None
+# Internal exports used only by the benchmark (not in obl.h): obl_linear with a
+# span record of the GEMV launch, and the measurement kernels of peaks.hip.
+lib.obl_internal_linear_span.argtypes = [_vp, _int, _i64, _i64, _vp, _i64, _vp, _vp, _int, _vp, _int, _vp, _vp]
+lib.obl_internal_linear_span.restype = _int
+lib.obl_internal_wallclock_khz.argtypes = []
+lib.obl_internal_wallclock_khz.restype = _int
+lib.obl_internal_peak_read.argtypes = [_vp, _i64, _vp, _vp]
+lib.obl_internal_peak_read.restype = _int
+lib.obl_internal_peak_mfma.argtypes = [_i64, _vp, ctypes.POINTER(ctypes.c_double), _vp]
+lib.obl_internal_peak_mfma.restype = _int
 
 _DT = {torch.float32: OBL_F32, torch.float16: OBL_F16, torch.bfloat16: OBL_BF16, torch.int8: OBL_I8}
 
@@ -368,3 +378,43 @@ def linear_layernorm(X: torch.Tensor, W_packed: torch.Tensor, a: torch.Tensor, b
                                     dtype_code(sdt), eps, _ptr(gamma), _ptr(beta), _ptr(workspace),
                                     _ptr(out), dtype_code(out.dtype), _stream(X)), "obl_linear_layernorm")
     return out, workspace
+
+
+# ---------------------------------------------------------------------------
+# Measurement hooks for the benchmark (internal exports, not part of obl.h).
+def linear_span(X: torch.Tensor, W_packed: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out: torch.Tensor,
+                span: torch.Tensor) -> torch.Tensor:
+    """``linear`` whose decode-GEMV launch (M <= 2) also records, per workgroup, its start and end in
+    constant-clock ticks into ``span`` (int64, at least 2 N entries, 16-byte aligned)."""
+    M, K = _mat(X, "X")
+    _dtype(X, "X", _XDT)
+    N = _mat(W_packed, "W_packed")[0]
+    _packed(W_packed, "W_packed", N, K)
+    sdt = _scales([(a, "a", N), (b, "b", K)], None)
+    out = _out(out, "out", (M, N), _YDT, torch.float32, X.device)
+    _dev(span, "span")
+    _dtype(span, "span", (torch.int64,))
+    if span.numel() < 2 * N:
+        raise ValueError("span must hold 2 N entries")
+    _check(lib.obl_internal_linear_span(_ptr(X), dtype_code(X.dtype), M, K, _ptr(W_packed), N, _ptr(a), _ptr(b),
+                                        dtype_code(sdt), _ptr(out), dtype_code(out.dtype), _ptr(span), _stream(X)),
+           "obl_internal_linear_span")
+    return out
+
+
+def peak_read(buf: torch.Tensor, sink: torch.Tensor):
+    """Streaming read of every byte of ``buf`` (measurement kernel); ``sink`` (int32, >= 8 per CU) is
+    never written in practice."""
+    _dev(buf, "buf")
+    _dev(sink, "sink")
+    _check(lib.obl_internal_peak_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf)),
+           "obl_internal_peak_read")
+
+
+def peak_mfma(iters: int, sink: torch.Tensor) -> float:
+    """Matrix-core loop (measurement kernel); returns the launch's dense flop count.  ``sink`` (fp32,
+    >= 512 per CU) is never written in practice."""
+    _dev(sink, "sink")
+    flops = ctypes.c_double(0.0)
+    _check(lib.obl_internal_peak_mfma(iters, _ptr(sink), ctypes.byref(flops), _stream(sink)), "obl_internal_peak_mfma")
+    return flops.value

@@ -21,7 +21,7 @@ LIB = os.path.join(LIBDIR, "libobl.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["obl_api.hip", "pack.hip", "gemv_lut.hip", "decode_mfma.hip", "gemm_mfma.hip", "gemm_wide.hip", "backward.hip", "svid.hip",
-           "layernorm.hip"]
+           "layernorm.hip", "peaks.hip"]
 ARCH = os.environ.get("OBL_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU ops (v_pk_*_f32) are disabled for device code.

@@ -93,7 +93,11 @@ template <int MR, int RPH, bool MULTI, typename XT, typename ST, typename YT, bo
 __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
     const XT* __restrict__ X, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const ST* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y,
-    int rows_per_block) {
+    int rows_per_block, uint64_t* __restrict__ span) {
+  // Start of this wave in constant-clock ticks; stored at the end only when
+  // a span record was asked for (the read is issued unconditionally: no
+  // branch, and its wait falls on the first LDS wait below).
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   // One 16-entry table per group and row.  MR = 2: lut[(nib * LUT_COLS + col)
   // * MR + m].  MR = 1: the paired layout (see lut_dw below).
   constexpr bool PAIRED = MR == 1;
@@ -320,6 +324,14 @@ __global__ __launch_bounds__(LUT_THREADS) void gemv_lut_kernel(
       for (int m = 0; m < MR; ++m) Store<YT>::put(&Y[m * N + n], tot[m] * post_r[r]);
     }
   }
+  if (span) {   // uniform: the block's start (wave 0) and end (after every wave's stores)
+    __syncthreads();
+    if (tid == 0) {
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+      *reinterpret_cast<u32x4*>(span + 2 * blockIdx.x) =
+          u32x4{(uint32_t)t_start, (uint32_t)(t_start >> 32), (uint32_t)t_end, (uint32_t)(t_end >> 32)};
+    }
+  }
 }
 
 template <int MR, int RPH, typename XT, typename ST, typename YT, bool PRE>
@@ -334,11 +346,11 @@ hipError_t launch_rph(const LinearArgs& a, int64_t blocks, int rpb) {
   const dim3 grid((unsigned)blocks), block(LUT_THREADS);
   const bool multi = a.K > LUT_SLAB_K;
   if (vec4 && !multi)
-    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, false, XT, ST, YT, PRE, true>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb);
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, false, XT, ST, YT, PRE, true>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb, a.span);
   else if (vec4)
-    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, true, XT, ST, YT, PRE, true>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb);
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, true, XT, ST, YT, PRE, true>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb, a.span);
   else
-    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, true, XT, ST, YT, PRE, false>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb);
+    hipLaunchKernelGGL((gemv_lut_kernel<MR, RPH, true, XT, ST, YT, PRE, false>), grid, block, 0, a.stream, X, a.K, a.W, a.N, pre, post, Y, rpb, a.span);
   return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ bool dims_ok(std::initializer_list<int64_t> dims) {
 // only; otherwise the path follows from M.
 enum Path { P_AUTO, P_LUT, P_DECODE, P_GEMM };
 thread_local ForcedKernels t_forced;
+thread_local uint64_t* t_span = nullptr;   // set only inside obl_internal_linear_span
 
 Path forced_path() {
   switch (t_forced.path) {
@@ -483,6 +484,7 @@ obl_status obl_linear(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
     if (st != OBL_OK) return st;
     if (M == 0) return OBL_OK;
     LinearArgs la{X, x_dtype, M, K, W_packed, N, b, a, scale_dtype, Y, y_dtype, (hipStream_t)stream};
+    la.span = t_span;
     return plan_and_run(la, path);
   } catch (...) {
     return OBL_ERR_INTERNAL;
@@ -712,6 +714,31 @@ obl_status dbf_linear_noalloc(const void* X, obl_dtype x_dtype, int64_t M, int64
                               float* workspace, void* Y, obl_dtype y_dtype, void* stream) {
   return dbf_impl(X, x_dtype, M, K, S2_packed, Kmid, S1_packed, N, b, m, a, scale_dtype, workspace, Y, y_dtype,
                   stream, SRC_FIXED);
+}
+
+// Internal export for the benchmark, not declared in obl.h: obl_linear whose
+// LUT GEMV launch (M <= 2) also writes a span record -- for each workgroup,
+// the constant-clock ticks (s_memrealtime) at its first wave's start and at
+// its end -- to span[2 * blocks], 16-byte aligned.  Other paths ignore span.
+obl_status obl_internal_linear_span(const void* X, obl_dtype x_dtype, int64_t M, int64_t K,
+                                    const uint32_t* W_packed, int64_t N, const void* a, const void* b,
+                                    obl_dtype scale_dtype, void* Y, obl_dtype y_dtype, uint64_t* span,
+                                    void* stream) {
+  if (!span || reinterpret_cast<uintptr_t>(span) % 16 != 0) return OBL_ERR_ALIGN;
+  t_span = span;
+  const obl_status st = obl_linear(X, x_dtype, M, K, W_packed, N, a, b, scale_dtype, Y, y_dtype, stream);
+  t_span = nullptr;
+  return st;
+}
+
+// Internal export for the benchmark, not declared in obl.h: the frequency of
+// the constant clock s_memrealtime counts (kHz) on the current device, or a
+// negative value on error.
+int obl_internal_wallclock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return -1;
+  return khz;
 }
 
 // Internal export for the test suite, not declared in obl.h: forces a path

@@ -26,6 +26,10 @@ struct LinearArgs {
   hipStream_t stream;
   const struct ScratchCtx* sx = nullptr;  // library scratch reserved for this call (see ScratchCtx)
   void* Y2 = nullptr; // optional bf16 copy of Y (prefill GEMM only; see gemm_wide_eligible)
+  // Optional span record (LUT GEMV only; the bench's kernel-time measurement):
+  // block b writes its first wave's start and its end, in s_memrealtime
+  // ticks, to span[2b], span[2b + 1].
+  uint64_t* span = nullptr;
   void* T3 = nullptr; // optional exact bf16 terms of an fp32 Y, [3][M][N] (decode whole-K kernel only)
   // Optional gradient epilogue (decode whole-K kernel only; the layer's
   // backward): gsum[n] = Σ_m gin[m][n] · Y[m][n] (gin in x_dtype, gsum fp32),
