@@ -37,7 +37,11 @@
  *    anything, and the capture stays valid: make one call of the same shape
  *    on that stream before capturing.  A captured graph uses the scratch of
  *    the stream it was captured on, so replays of graphs captured on one
- *    stream must not overlap each other in time.
+ *    stream must not overlap each other, or calls on that stream, in time.
+ *    Each stream that has made a call needing scratch keeps its pool (at
+ *    least 4 MiB per buffer in use) until the process ends, so a program
+ *    that runs such calls on many short-lived streams holds memory for
+ *    each of them.
  *  - Errors: every argument is validated BEFORE any HIP call; a failed check
  *    returns its status and enqueues nothing.  No call aborts or throws across
  *    the ABI.  HIP failures (including launch failures seen through
