@@ -71,3 +71,33 @@ def test_noalloc_refuses_more_than_the_array():
     assert e.value.status == B.OBL_ERR_SCRATCH
     torch.cuda.synchronize()
     assert bool((Y == 7.0).all())
+
+
+@pytest.mark.parametrize("M,K,Kmid,N,y_dtype", [(8, 4096, 3072, 4096, torch.float32),
+                                                (512, 4096, 3072, 4096, torch.bfloat16)])
+def test_noalloc_in_graph_on_a_fresh_stream(M, K, Kmid, N, y_dtype):
+    """The allocation-free call captured on a stream the library has never
+    seen (so it has no per-stream scratch): every replay, with unrelated eager
+    work between replays, equals the eager result bitwise."""
+    G.say(f"noalloc graph M={M} K={K} Kmid={Kmid} N={N}")
+    c = WL.dbf_case(M, K, Kmid, N, seed=29)
+    X, S2, S1, sc = _dev_case(c)
+    ws = torch.empty((M, Kmid), dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, N), dtype=y_dtype, device="cuda")
+    B.dbf_linear_noalloc(X, S2, S1, *sc, workspace=ws, out=Y)   # eager, on the current stream
+    torch.cuda.synchronize()
+    ref_y, ref_ws = Y.clone(), ws.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.dbf_linear_noalloc(X, S2, S1, *sc, workspace=ws, out=Y)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        Y.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        (torch.randn(1 << 20, device="cuda") * 2).sum().item()   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref_y), f"replay {rep}: output differs from the eager call"
+        assert torch.equal(ws, ref_ws), f"replay {rep}: workspace differs from the eager call"
