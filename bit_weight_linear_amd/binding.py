@@ -62,7 +62,7 @@ lib.obl_version.argtypes = []
 lib.obl_version.restype = _int
 # Internal export used only by the test suite (not in obl.h): forces a path and
 # kernel for the calling thread; see forced_kernels below.
-lib.obl_internal_force_kernels.argtypes = [_int, _int, _int]
+lib.obl_internal_force_kernels.argtypes = [_int, _int, _int, _int]
 lib.obl_internal_force_kernels.restype = None
 # Internal exports used only by the benchmark (not in obl.h): obl_linear with a
 # span record of the GEMV launch, and the measurement kernels of peaks.hip.
@@ -180,30 +180,34 @@ def _out(t: Optional[torch.Tensor], name: str, shape, dtypes, default_dtype, dev
 _PATHS = {None: 0, "auto": 0, "lut": 1, "decode": 2, "gemm": 3}
 _GEMMS = {None: 0, "auto": 0, "v1": 1, "v2": 2, "w1": 11, "w2": 12, "w4": 14, "w7": 17}
 _DECODES = {None: 0, "auto": 0, "split": 1, "wk1": 11, "wk2": 12, "wk4": 14}
+_PAIRS = {None: 0, "auto": 0, "off": 1}
 
 
 _forced = threading.local()
 
 
 def _forced_state():
-    return getattr(_forced, "state", {"path": None, "gemm": None, "decode": None})
+    return getattr(_forced, "state", {"path": None, "gemm": None, "decode": None, "pair": None})
 
 
 def _apply_forced(state):
     _forced.state = dict(state)
-    lib.obl_internal_force_kernels(_PATHS[state["path"]], _GEMMS[state["gemm"]], _DECODES[state["decode"]])
+    lib.obl_internal_force_kernels(_PATHS[state["path"]], _GEMMS[state["gemm"]], _DECODES[state["decode"]],
+                                   _PAIRS[state["pair"]])
 
 
 @contextlib.contextmanager
-def forced_kernels(path: Optional[str] = None, gemm: Optional[str] = None, decode: Optional[str] = None):
+def forced_kernels(path: Optional[str] = None, gemm: Optional[str] = None, decode: Optional[str] = None,
+                   pair: Optional[str] = None):
     """Test-suite hook: force a path ("lut" | "decode" | "gemm"), a prefill kernel or tile ("v1", "v2",
-    "w1", "w2", "w4", "w7") and a decode kernel ("split", "wk1", "wk2", "wk4") for this thread's calls
-    inside the block (nested blocks combine; arguments left None keep the enclosing choice), through an
-    internal export that obl.h does not declare.  Nothing else reaches it: ordinary calls always run
-    the kernel their arguments select."""
+    "w1", "w2", "w4", "w7"), a decode kernel ("split", "wk1", "wk2", "wk4") and whether the backward
+    may run its two contractions as one launch ("off": two launches) for this thread's calls inside the
+    block (nested blocks combine; arguments left None keep the enclosing choice), through an internal
+    export that obl.h does not declare.  Nothing else reaches it: ordinary calls always run the kernel
+    their arguments select."""
     old = _forced_state()
     new = dict(old)
-    for k, v in (("path", path), ("gemm", gemm), ("decode", decode)):
+    for k, v in (("path", path), ("gemm", gemm), ("decode", decode), ("pair", pair)):
         if v is not None:
             new[k] = v
     _apply_forced(new)

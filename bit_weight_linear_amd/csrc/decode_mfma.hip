@@ -457,8 +457,11 @@ __device__ __forceinline__ void wk_wave_sync() {
 // backward (bf16 gin): gsum[n] = Σ_m gin[m][n] · y[m][n] over the block's
 // rows in order, and, with gout, gout[m][n] = y[m][n] · gscale[n] (fp32 or
 // bf16 as gout_bf16 says).
+// The body of one workgroup: `bx` is its block index within its problem and
+// wk_lds the workgroup's dynamic LDS.
 template <int XM, typename ST, typename YT, int CPW, int PER, bool NT, bool MS>
-__global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
+__device__ __forceinline__ void decode_wk_body(
+    u32x4* wk_lds, unsigned bx,
     const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
     const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3,
     const bf16_t* __restrict__ gin, float* __restrict__ gsum, const ST* __restrict__ gscale,
@@ -476,7 +479,6 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
   constexpr int NOUT = (16 * RF * NC + THREADS - 1) / THREADS;    // final outputs per thread
   constexpr bool SL = wk_signs_in_lds(XM, PER, CPW);              // sign words by DMA into LDS
   constexpr int XD = TT * PER;                                    // X DMAs per k-quarter
-  extern __shared__ u32x4 wk_lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
   const int g = lane >> 4;
   const int64_t kw = K >> 5;
   const int nslices = (int)((kw + DEC_STEPS - 1) / DEC_STEPS);
-  const int64_t n0 = (int64_t)blockIdx.x * NC;
+  const int64_t n0 = (int64_t)bx * NC;
   u32x4* xw = wk_lds + (size_t)wave * wk_wave_units(XM, PER, CPW);   // X terms and quarters
   u32x4* mq = xw + TT * TS;                                       // WK_B2: b_hi quads [64], b_lo quads [64]
   uint32_t* mw = reinterpret_cast<uint32_t*>(mq);
@@ -801,6 +803,53 @@ __global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
   }
 }
 
+template <int XM, typename ST, typename YT, int CPW, int PER, bool NT, bool MS>
+__global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_kernel(
+    const bf16_t* __restrict__ X, int M, int64_t K, const uint32_t* __restrict__ W, int64_t N,
+    const f16_t* __restrict__ pre, const ST* __restrict__ post, YT* __restrict__ Y, bf16_t* __restrict__ T3,
+    const bf16_t* __restrict__ gin, float* __restrict__ gsum, const ST* __restrict__ gscale,
+    void* __restrict__ gout, int gout_bf16) {
+  extern __shared__ u32x4 wk_lds[];
+  decode_wk_body<XM, ST, YT, CPW, PER, NT, MS>(wk_lds, blockIdx.x, X, M, K, W, N, pre, post, Y, T3, gin, gsum,
+                                               gscale, gout, gout_bf16);
+}
+
+// The arguments of one whole-K problem (as decode_wk_kernel takes them).
+template <typename ST, typename YT>
+struct WkProb {
+  const bf16_t* X;
+  int M;
+  int64_t K;
+  const uint32_t* W;
+  int64_t N;
+  const f16_t* pre;
+  const ST* post;
+  YT* Y;
+  bf16_t* T3;
+  const bf16_t* gin;
+  float* gsum;
+  const ST* gscale;
+  void* gout;
+  int gout_bf16;
+};
+
+// Two problems of one kernel instance in one launch (the backward's two
+// contractions): blocks [0, nb0) take p0, the others p1.  A workgroup's
+// result does not depend on which launch it belongs to.
+template <int XM, typename ST, typename YT, int CPW, int PER, bool NT, bool MS>
+__global__ __launch_bounds__(64 * wk_waves(XM, PER, CPW)) void decode_wk_pair_kernel(WkProb<ST, YT> p0,
+                                                                                    WkProb<ST, YT> p1,
+                                                                                    unsigned nb0) {
+  extern __shared__ u32x4 wk_lds[];
+  if (blockIdx.x < nb0)
+    decode_wk_body<XM, ST, YT, CPW, PER, NT, MS>(wk_lds, blockIdx.x, p0.X, p0.M, p0.K, p0.W, p0.N, p0.pre, p0.post,
+                                                 p0.Y, p0.T3, p0.gin, p0.gsum, p0.gscale, p0.gout, p0.gout_bf16);
+  else
+    decode_wk_body<XM, ST, YT, CPW, PER, NT, MS>(wk_lds, blockIdx.x - nb0, p1.X, p1.M, p1.K, p1.W, p1.N, p1.pre,
+                                                 p1.post, p1.Y, p1.T3, p1.gin, p1.gsum, p1.gscale, p1.gout,
+                                                 p1.gout_bf16);
+}
+
 template <int XM, typename ST, typename YT, int CPW, int PER, bool NT = true, bool MS = false>
 hipError_t launch_wk(const LinearArgs& a) {
   if constexpr (XM == WK_B2 && NT) {
@@ -874,6 +923,36 @@ hipError_t launch_wk_any(const LinearArgs& a, int cpw) {
 
 // K-slices of the split kernel.
 int64_t split_slices(const LinearArgs& a) { return (a.K / 32 + DEC_STEPS - 1) / DEC_STEPS; }
+
+// The backward's pair in one launch: mode B2, fp16 scales, fp32 outputs, plain
+// sign loads (NT = false, as launch_wk picks for a gradient epilogue).
+template <int CPW, int PER, bool MS>
+hipError_t launch_pair_t(const LinearArgs& t, const LinearArgs& u, int64_t nb0, int64_t nb1) {
+  auto prob = [](const LinearArgs& a) {
+    return WkProb<f16_t, float>{static_cast<const bf16_t*>(a.X), (int)a.M, a.K, a.W, a.N,
+                                static_cast<const f16_t*>(a.pre), static_cast<const f16_t*>(a.post),
+                                static_cast<float*>(a.Y), static_cast<bf16_t*>(a.T3),
+                                static_cast<const bf16_t*>(a.gin), a.gsum, static_cast<const f16_t*>(a.gscale),
+                                a.gout, a.gout_dtype == DT_BF16 ? 1 : 0};
+  };
+  hipLaunchKernelGGL((decode_wk_pair_kernel<WK_B2, f16_t, float, CPW, PER, false, MS>), dim3((unsigned)(nb0 + nb1)),
+                     dim3(64 * wk_waves(WK_B2, PER, CPW)), wk_lds_bytes(WK_B2, PER, CPW), t.stream, prob(t), prob(u),
+                     (unsigned)nb0);
+  return hipGetLastError();
+}
+
+template <int CPW, int PER>
+hipError_t launch_pair_ms(const LinearArgs& t, const LinearArgs& u, int64_t nb0, int64_t nb1, bool ms) {
+  return ms ? launch_pair_t<CPW, PER, true>(t, u, nb0, nb1) : launch_pair_t<CPW, PER, false>(t, u, nb0, nb1);
+}
+
+template <int CPW>
+hipError_t launch_pair_per(const LinearArgs& t, const LinearArgs& u, int64_t nb0, int64_t nb1, int per, bool ms) {
+  if (per == 1) return launch_pair_ms<CPW, 1>(t, u, nb0, nb1, ms);
+  if (per == 2) return launch_pair_ms<CPW, 2>(t, u, nb0, nb1, ms);
+  if (per == 4) return launch_pair_ms<CPW, 4>(t, u, nb0, nb1, ms);
+  return launch_pair_ms<CPW, 8>(t, u, nb0, nb1, ms);
+}
 
 template <int MODE, typename XT, typename ST, typename YT, bool PRE>
 hipError_t launch_t(const LinearArgs& a, const DeviceInfo& dev) {
@@ -972,6 +1051,39 @@ bool decode_terms_ok(const LinearArgs& s1, const LinearArgs& s2) {
   LinearArgs t = s2;
   t.X = s2.W;   // the terms go to 256-byte aligned library scratch: only sizes and W are checked
   return wk_operands_ok(t, 3);
+}
+
+hipError_t launch_decode_pair(const LinearArgs& t, const LinearArgs& u, const DeviceInfo& dev) {
+  const auto plain = [](const LinearArgs& a) {
+    return a.x_dtype == DT_BF16 && a.scale_dtype == DT_F16 && a.y_dtype == DT_F32 && a.gsum && !a.T3 && !a.Y2 &&
+           decode_wide_ok(a);
+  };
+  if (t.M != u.M || t.stream != u.stream || !plain(t) || !plain(u)) return hipErrorNotSupported;
+  // Columns per wave: a forced whole-K variant for both, else the fewest that
+  // keep the two grids together within one workgroup per CU.
+  const int forced = forced_kernels().decode;
+  int cpw = forced > 10 ? forced - 10 : 0;
+  const int64_t ct = (t.N + 15) / 16, cu = (u.N + 15) / 16;
+  if (cpw == 0) {
+    cpw = 4;
+    for (int c = 1; c <= 2; c *= 2)
+      if ((ct + c - 1) / c + (cu + c - 1) / c <= dev.num_cus) {
+        cpw = c;
+        break;
+      }
+  }
+  if (cpw != 1 && cpw != 2 && cpw != 4) return hipErrorNotSupported;
+  const int per = wk_per(t.M);
+  const int waves = wk_waves(WK_B2, per, cpw);
+  // One instance for both: the same choice of the compensated per-slice fold.
+  const bool ms_t = (t.K / 32 + DEC_STEPS - 1) / DEC_STEPS > waves;
+  const bool ms_u = (u.K / 32 + DEC_STEPS - 1) / DEC_STEPS > waves;
+  if (ms_t != ms_u || t.M > 4 * per) return hipErrorNotSupported;
+  const int64_t nb0 = (t.N + 16 * cpw - 1) / (16 * cpw), nb1 = (u.N + 16 * cpw - 1) / (16 * cpw);
+  if (nb0 + nb1 > 0x7fffffff) return hipErrorNotSupported;
+  if (cpw == 1) return launch_pair_per<1>(t, u, nb0, nb1, per, ms_t);
+  if (cpw == 2) return launch_pair_per<2>(t, u, nb0, nb1, per, ms_t);
+  return launch_pair_per<4>(t, u, nb0, nb1, per, ms_t);
 }
 
 bool decode_wide_ok(const LinearArgs& a) {

@@ -618,6 +618,12 @@ obl_status obl_linear_backward(const void* dY, const void* X, obl_dtype x_dtype,
     ScratchCtx sx;
     if ((st = acquire_scratch(SRC_POOL, dev, hs, need, &sx)) != OBL_OK) return st;
     t.sx = u.sx = &sx;
+    if (fused && t_forced.pair != 1) {
+      // Both contractions in one launch where they take one kernel instance.
+      const hipError_t e = launch_decode_pair(t, u, dev);
+      if (e == hipSuccess) return hipGetLastError() == hipSuccess ? OBL_OK : OBL_ERR_HIP;
+      if (e != hipErrorNotSupported) return OBL_ERR_HIP;
+    }
     st = run_linear(t, path, dev);
     if (st != OBL_OK) return st;
     st = run_linear(u, path, dev);
@@ -746,10 +752,11 @@ int obl_internal_wallclock_khz(void) {
 // calling thread's later calls; all zeros restores the automatic choice.
 // Nothing else reads or sets it, so ordinary callers always get the kernel
 // their arguments select.
-void obl_internal_force_kernels(int path, int gemm, int decode) {
+void obl_internal_force_kernels(int path, int gemm, int decode, int pair) {
   t_forced.path = path;
   t_forced.gemm = gemm;
   t_forced.decode = decode;
+  t_forced.pair = pair;
 }
 
 }  // extern "C"

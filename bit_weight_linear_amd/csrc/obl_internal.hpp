@@ -103,6 +103,11 @@ bool decode_wide_preferred(const LinearArgs& a);
 // A DBF decode can run both stages on the whole-K kernel: stage 1 writes the
 // exact bf16 terms of T1 (s1.T3), stage 2 reads them (x_dtype DT_BF16X3).
 bool decode_terms_ok(const LinearArgs& s1, const LinearArgs& s2);
+// Two whole-K contractions with gradient epilogues (the layer's backward: bf16
+// x, fp16 scales, fp32 outputs, same M and stream) as one launch; returns
+// hipErrorNotSupported, with nothing launched, when they do not take one
+// kernel instance.
+hipError_t launch_decode_pair(const LinearArgs& t, const LinearArgs& u, const DeviceInfo& dev);
 hipError_t launch_gemm_mfma(const LinearArgs& a, const DeviceInfo& dev);
 // Scratch the prefill path's launch of this call takes (prescaled
 // activations in slot 0, split-K partial sums in slot 1).
@@ -126,9 +131,10 @@ void gemm_wide_prescaled_scratch(const LinearArgs& a, const DeviceInfo& dev, Scr
 // gemm: 0 auto, 1 / 2 the older 8-wave / LDS-staged kernels, 11 / 12 / 14 /
 // 17 a tile of the main kernel (64 x 128, 128 x 128, 128 x 256, 128 x 448).
 // decode: 0 auto, 1 the split kernel, 11 / 12 / 14 the whole-K kernel with
-// 1 / 2 / 4 column groups per wave.
+// 1 / 2 / 4 column groups per wave.  pair: 0 auto, 1 the backward's two
+// contractions as two launches.
 struct ForcedKernels {
-  int path = 0, gemm = 0, decode = 0;
+  int path = 0, gemm = 0, decode = 0, pair = 0;
 };
 const ForcedKernels& forced_kernels();
 

@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture
 def forcer():
-    """forcer(path=..., gemm=..., decode=...): force kernels for the rest of the test (the library's
+    """forcer(path=..., gemm=..., decode=..., pair=...): force kernels for the rest of the test (the library's
     test-only hook, per thread); the automatic choice is restored at teardown."""
     stack = []
 

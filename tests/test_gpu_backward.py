@@ -123,3 +123,48 @@ def test_backward_fused_epilogue_column_groups(impl, forcer):
     assert O.max_normalised_error(dX, rdX, sdx) <= G.TOL_DECODE + G.BF16_U
     assert O.max_normalised_error(da, rda, sda) <= G.TOL_DECODE
     assert O.max_normalised_error(db, rdb, sdb) <= G.TOL_DECODE
+
+
+# Shapes whose two contractions share one whole-K kernel instance run as one
+# launch: square and oblong layers, 17..32 rows (four waves), and K = 32768
+# against N = 4096 (the two contractions need different instances: two
+# launches).  With the column groups per wave forced, one launch and two run
+# the same workgroups and must agree bitwise; by default the pair picks its
+# own column count (both grids within one workgroup per CU), which changes the
+# order of the fp32 adds, so it is held to the oracle's bound.
+PAIR_CASES = [(16, 4096, 4096), (5, 1024, 512), (8, 2048, 4096), (3, 4096, 11008), (24, 1152, 640),
+              (32, 4096, 4096), (4, 32768, 4096)]
+
+
+def _oracle_bounds(X, dY, S, a, b, got, dx_dtype):
+    rdX, rda, rdb = O.onebit_backward(X, S, a, b, dY)
+    sdx, sda, sdb = O.backward_error_scales(X, a, b, dY)
+    tol_dx = G.TOL_DECODE + (G.BF16_U if dx_dtype == "bf16" else 0.0)
+    assert O.max_normalised_error(got[0], rdX, sdx) <= tol_dx
+    assert O.max_normalised_error(got[1], rda, sda) <= G.TOL_DECODE
+    assert O.max_normalised_error(got[2], rdb, sdb) <= G.TOL_DECODE
+
+
+@pytest.mark.parametrize("M,K,N", PAIR_CASES)
+@pytest.mark.parametrize("impl", ["wk1", "wk2"])
+def test_backward_one_launch_equals_two(M, K, N, impl, forcer):
+    """Same column groups per wave: the one-launch backward gives bitwise the
+    dX, da, db and workspace of two launches."""
+    forcer(decode=impl)
+    G.say(f"backward one vs two launches M={M} K={K} N={N} {impl}")
+    X, dY, S, a, b = _case(M, K, N, "bf16", "f16", seed=M * 3 + K + N)
+    one = _run(X, dY, S, a, b, "bf16", "f16", "f32")
+    with B.forced_kernels(pair="off"):
+        two = _run(X, dY, S, a, b, "bf16", "f16", "f32")
+    for u, v, what in zip(one[:3], two[:3], ("dX", "da", "db")):
+        assert np.array_equal(u, v), f"{what} differs between one and two launches"
+    assert torch.equal(one[3], two[3]), "workspace differs between one and two launches"
+    _oracle_bounds(X, dY, S, a, b, one, "f32")
+
+
+@pytest.mark.parametrize("M,K,N", PAIR_CASES)
+@pytest.mark.parametrize("dx_dtype", ["f32", "bf16"])
+def test_backward_default_pairing_against_oracle(M, K, N, dx_dtype):
+    G.say(f"backward default pairing M={M} K={K} N={N} dX {dx_dtype}")
+    X, dY, S, a, b = _case(M, K, N, "bf16", "f16", seed=M * 5 + K + N)
+    _oracle_bounds(X, dY, S, a, b, _run(X, dY, S, a, b, "bf16", "f16", dx_dtype), dx_dtype)
